@@ -1,0 +1,178 @@
+"""CPU oracle for the packed varlen causal depthwise width-4 convolution.
+
+TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU
+baseline leg of ``bench.py`` may import this package. The product path (the HIP
+library and its Python binding) never does, and shares no code with it.
+
+The arithmetic lives in ``kdaconv_oracle.c`` (plain single-threaded C, built by
+:func:`build` with gcc, no fast-math, no FP contraction). This module only
+marshals numpy arrays into it. What it computes, and the readings taken where
+the page "vllm.models.kimi_k3.nvidia.ops.kda_conv" is silent, are stated in the
+C file's header.
+
+Pins (tests/test_oracle_*.py): exhaustive bf16 rounding against torch's CPU
+conversion; the correctly rounded exp against mpmath; the SiLU map against exact
+rational arithmetic; the conv against exact-rational brute force, hand-derived
+golden cases, invariants, and PyTorch's float64 conv1d within its error bound.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import pathlib
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = pathlib.Path(__file__).resolve().parent
+SOURCE = _HERE / "kdaconv_oracle.c"
+LIBRARY = _HERE / "libkdaconv_oracle.so"
+
+_CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math",
+           "-Wall", "-Wextra"]
+
+
+def build(output: Optional[pathlib.Path] = None, extra_flags: tuple = ()) -> pathlib.Path:
+    """Compile the oracle with gcc into a shared library and return its path."""
+    out = pathlib.Path(output) if output is not None else LIBRARY
+    tmp = out.with_name(out.name + f".tmp{os.getpid()}")
+    cmd = ["gcc", *_CFLAGS, *extra_flags, "-o", str(tmp), str(SOURCE), "-lquadmath", "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+_lib = None
+
+
+def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
+    i64, i32, f32 = ctypes.c_int64, ctypes.c_int, ctypes.c_float
+    vp = ctypes.c_void_p
+    lib.oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]
+    lib.oracle_bf16_to_f32.restype = f32
+    lib.oracle_f32_to_bf16.argtypes = [f32]
+    lib.oracle_f32_to_bf16.restype = ctypes.c_uint16
+    lib.oracle_crexpf.argtypes = [f32]
+    lib.oracle_crexpf.restype = f32
+    lib.oracle_crexpf_escalates.argtypes = [f32]
+    lib.oracle_crexpf_escalates.restype = i32
+    lib.oracle_act_bf16.argtypes = [f32, i32]
+    lib.oracle_act_bf16.restype = ctypes.c_uint16
+    lib.oracle_act_bf16_range.argtypes = [ctypes.c_uint32, ctypes.c_uint64, i32, vp]
+    lib.oracle_act_bf16_range.restype = None
+    lib.oracle_act_bf16_list.argtypes = [vp, ctypes.c_uint64, i32, vp]
+    lib.oracle_act_bf16_list.restype = None
+    lib.oracle_crexpf_scan.argtypes = [ctypes.c_uint32, ctypes.c_uint64, vp, ctypes.c_uint64,
+                                       ctypes.POINTER(ctypes.c_double)]
+    lib.oracle_crexpf_scan.restype = ctypes.c_uint64
+    lib.oracle_packed_causal_conv1d.argtypes = [
+        vp, i64, i64, i64,  # x, num_tokens, dim, x_row_stride
+        vp, i64, i64, vp,  # weight, w_stride0, w_stride1, bias
+        vp, i64, i64, i64, i64,  # conv_states, lines, strides
+        vp, i64,  # query_start_loc, num_seqs
+        vp, i64, vp,  # cache_indices, ci_stride, has_initial_state
+        i64, i32, i32, i64,  # part_dim, silu, has_null_block, null_block_id
+        vp,  # out
+    ]
+    lib.oracle_packed_causal_conv1d.restype = i32
+    return lib
+
+
+def load(path: Optional[pathlib.Path] = None) -> ctypes.CDLL:
+    """Load (building first if absent) the oracle library."""
+    global _lib
+    if path is not None:
+        return _bind(ctypes.CDLL(str(path)))
+    if _lib is None:
+        if not LIBRARY.exists():
+            build()
+        _lib = _bind(ctypes.CDLL(str(LIBRARY)))
+    return _lib
+
+
+def is_silu(activation) -> bool:
+    """The page's activation rule: "silu", "swish" or True select SiLU, anything else none."""
+    return activation in ("silu", "swish", True)
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data
+
+
+def crexpf(x, lib=None) -> np.ndarray:
+    lib = lib or load()
+    xs = np.asarray(x, dtype=np.float32).ravel()
+    return np.array([lib.oracle_crexpf(float(v)) for v in xs], dtype=np.float32)
+
+
+def act_bf16(a, silu: bool, lib=None) -> np.ndarray:
+    """Stored bf16 word for each FP32 accumulator value in ``a``."""
+    lib = lib or load()
+    bits = np.ascontiguousarray(np.asarray(a, dtype=np.float32).ravel()).view(np.uint32)
+    out = np.empty(bits.size, dtype=np.uint16)
+    lib.oracle_act_bf16_list(bits.ctypes.data, bits.size, int(silu), out.ctypes.data)
+    return out
+
+
+def act_bf16_range(first: int, count: int, silu: bool, lib=None,
+                   out: Optional[np.ndarray] = None) -> np.ndarray:
+    """Stored bf16 word for the FP32 bit patterns first, first+1, ..., first+count-1."""
+    lib = lib or load()
+    if out is None:
+        out = np.empty(count, dtype=np.uint16)
+    assert out.dtype == np.uint16 and out.flags.c_contiguous and out.size >= count
+    lib.oracle_act_bf16_range(first & 0xFFFFFFFF, count, int(silu), out.ctypes.data)
+    return out
+
+
+def packed_causal_conv1d(x: np.ndarray, dim: int, weight: np.ndarray, bias: Optional[np.ndarray],
+                         conv_states: np.ndarray, query_start_loc: np.ndarray,
+                         cache_indices: np.ndarray, has_initial_state: Optional[np.ndarray],
+                         part_dim: int, activation="silu", null_block_id: Optional[int] = None,
+                         out: Optional[np.ndarray] = None, lib=None) -> np.ndarray:
+    """Run the oracle. ``conv_states`` is updated in place; returns ``out``.
+
+    x: uint16 bf16 bits (num_tokens, row_stride) with unit column stride, the op
+    reads columns [0, dim). Returns uint16 (dim // part_dim, num_tokens, part_dim);
+    rows that no sequence owns keep what ``out`` held (zeros when allocated here).
+    """
+    lib = lib or load()
+    assert x.dtype == np.uint16 and x.ndim == 2 and x.strides[1] == 2
+    assert weight.dtype == np.float32 and weight.ndim == 2 and weight.shape == (dim, 4)
+    assert conv_states.dtype == np.float32 and conv_states.ndim == 3
+    assert conv_states.shape[1] == dim and conv_states.shape[2] == 3
+    assert query_start_loc.dtype == np.int32 and cache_indices.dtype == np.int32
+    if bias is not None:
+        assert bias.dtype == np.float32 and bias.shape == (dim,) and bias.flags.c_contiguous
+    qsl = np.ascontiguousarray(query_start_loc)
+    init = None
+    if has_initial_state is not None:
+        init = np.ascontiguousarray(has_initial_state.astype(np.uint8))
+    T = x.shape[0]
+    if out is None:
+        out = np.zeros((dim // part_dim, T, part_dim), dtype=np.uint16)
+    assert out.dtype == np.uint16 and out.flags.c_contiguous
+    assert out.shape == (dim // part_dim, T, part_dim)
+    S = qsl.shape[0] - 1
+    rc = lib.oracle_packed_causal_conv1d(
+        x.ctypes.data, T, dim, x.strides[0] // 2,
+        weight.ctypes.data, weight.strides[0] // 4, weight.strides[1] // 4, _ptr(bias),
+        conv_states.ctypes.data, conv_states.shape[0], conv_states.strides[0] // 4,
+        conv_states.strides[1] // 4, conv_states.strides[2] // 4,
+        qsl.ctypes.data, S, cache_indices.ctypes.data, cache_indices.strides[0] // 4,
+        _ptr(init), part_dim, int(is_silu(activation)), int(null_block_id is not None),
+        0 if null_block_id is None else int(null_block_id), out.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle rejected the call (bad shapes or metadata)")
+    return out
+
+
+def run_workload(wl, out: Optional[np.ndarray] = None, lib=None):
+    """Run the oracle on a ``workloads.Workload``; returns (out, updated conv_states copy)."""
+    st = wl.conv_states.copy()
+    o = packed_causal_conv1d(wl.x, wl.dim, wl.weight, wl.bias, st, wl.query_start_loc,
+                             wl.cache_indices, wl.has_initial_state, wl.part_dim,
+                             wl.activation, wl.null_block_id, out=out, lib=lib)
+    return o, st

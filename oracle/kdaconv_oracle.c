@@ -1,0 +1,257 @@
+/*
+ * CPU oracle for the packed varlen causal depthwise width-4 convolution.
+ *
+ * TEST INFRASTRUCTURE. Only the tests, the smoke check and the bench's CPU
+ * baseline load this file's library. It is plain, single-threaded and slow on
+ * purpose, shares no code with the HIP path and is the definition the HIP path
+ * is held to, bit for bit.
+ *
+ * What it computes comes from the page "vllm.models.kimi_k3.nvidia.ops.kda_conv":
+ *   - module docstring, second paragraph: bf16 input widened to FP32 exactly,
+ *     the stock conv arithmetic in FP32 with FP32 weights and FP32 conv state,
+ *     SiLU, FP32 -> bf16 rounding to nearest even, output as dense
+ *     (tokens, part_dim) planes;
+ *   - module docstring, third paragraph: a sequence's conv state is read at its
+ *     first token and the updated state written back once;
+ *   - packed_causal_conv1d_fn docstring: semantics of causal_conv1d_fn on x.T,
+ *     conv_states of shape (cache lines, dim, 3) updated in place, width-4
+ *     taps, plane i holds channels [i*part_dim, (i+1)*part_dim);
+ *   - packed_causal_conv1d_fn source: activation "silu"/"swish"/True selects
+ *     SiLU; a null block id disables the state of the sequences mapped to it.
+ *
+ * Readings taken where the page is silent (each is listed in the design doc):
+ *   - tap 3 multiplies the current token, tap 0 the token three back (causal
+ *     conv as a left-padded cross-correlation);
+ *   - state index 0 is the oldest of the three history values;
+ *   - accumulation: start from the bias (or +0.0f), then one fused
+ *     multiply-add per tap, oldest tap first;
+ *   - SiLU is a / (1 + exp(-a)) with exp correctly rounded to binary32 and the
+ *     add and the divide rounded to binary32 (round to nearest even);
+ *   - a NaN result becomes the canonical bf16 quiet NaN 0x7FC0;
+ *   - a sequence whose cache line is the null block runs from zero history and
+ *     neither reads nor writes the state; has_initial_state false runs from
+ *     zero history and still writes the state;
+ *   - a zero-length sequence does nothing.
+ *
+ * Build: gcc -O2 -ffp-contract=off -fno-fast-math (see oracle/__init__.py).
+ */
+#include <math.h>
+#include <quadmath.h>
+#include <stdint.h>
+#include <string.h>
+
+#define ORACLE_OK 0
+#define ORACLE_EINVAL 1
+
+static uint32_t bits_of(float f) {
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  return u;
+}
+
+static float float_of(uint32_t u) {
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return f;
+}
+
+/* bf16 -> FP32. A bf16 number is the upper half of the FP32 word with the
+ * same value, so the widening is exact. */
+float oracle_bf16_to_f32(uint16_t h) { return float_of((uint32_t)h << 16); }
+
+/* FP32 -> bf16, round to nearest, ties to even. bf16 keeps the upper 16 bits
+ * of the FP32 word; the lower 16 bits decide the rounding. Values past the
+ * largest bf16 round to infinity by the same rule (the carry runs into the
+ * exponent). NaN becomes the quiet NaN 0x7FC0. */
+uint16_t oracle_f32_to_bf16(float y) {
+  if (isnan(y)) return 0x7FC0;
+  uint32_t u = bits_of(y);
+  uint32_t kept = u >> 16;       /* truncation toward zero */
+  uint32_t dropped = u & 0xFFFFu; /* fraction of one bf16 ulp, in 1/65536 */
+  if (dropped > 0x8000u || (dropped == 0x8000u && (kept & 1u))) kept += 1;
+  return (uint16_t)kept;
+}
+
+/* Midpoint test for the correctly rounded exp below: nonzero when the double
+ * value e lies within 2^-40 * e of a point halfway between two adjacent binary32
+ * numbers (2^128 counts as the number above FLT_MAX). */
+static int near_binary32_midpoint(double e) {
+  if (!(e > 0.0) || isinf(e) || e >= 0x1p129) return 0;
+  float r = (float)e;
+  float below;
+  if (isinf(r)) {
+    below = 0x1.fffffep127f;
+  } else if ((double)r > e) {
+    below = nextafterf(r, 0.0f);
+  } else {
+    below = r;
+  }
+  float up = nextafterf(below, INFINITY);
+  double above = isinf(up) ? 0x1p128 : (double)up;
+  double mid = 0.5 * ((double)below + above); /* exact in double */
+  return fabs(e - mid) <= 0x1p-40 * e;
+}
+
+/* exp(x) correctly rounded to binary32, round to nearest even.
+ *
+ * Method (the two-step scheme of the CORE-MATH project, Sibidanov, Zimmermann
+ * and Glondu, ARITH 2022, written here from its description): evaluate exp in
+ * double precision, whose relative error (libm, well under 2^-50) is far below
+ * the half-ulp of binary32, and round that to binary32. The rounding can only go
+ * wrong when the double value sits within its error of a binary32 midpoint; for
+ * those inputs the value is recomputed in 113-bit quad precision (libquadmath)
+ * and rounded from there. oracle/certify_expf.py checks the result against
+ * mpmath at 160 bits on every input the midpoint test catches and on a random
+ * sample of the rest. */
+float oracle_crexpf(float x) {
+  if (isnan(x)) return x + x;
+  double e = exp((double)x);
+  if (near_binary32_midpoint(e)) {
+    __float128 q = expq((__float128)x);
+    return (float)q;
+  }
+  return (float)e;
+}
+
+/* Nonzero when oracle_crexpf(x) took the quad-precision branch. */
+int oracle_crexpf_escalates(float x) {
+  if (isnan(x)) return 0;
+  return near_binary32_midpoint(exp((double)x));
+}
+
+/* The map from an FP32 accumulator to the stored bf16 word: SiLU
+ * y = a / (1 + exp(-a)) with each operation rounded to binary32 (or y = a when
+ * silu == 0), then bf16 rounding. */
+uint16_t oracle_act_bf16(float a, int silu) {
+  float y = a;
+  if (silu) {
+    float e = oracle_crexpf(-a);
+    float d = 1.0f + e;
+    y = a / d;
+  }
+  return oracle_f32_to_bf16(y);
+}
+
+/* oracle_act_bf16 over count consecutive FP32 bit patterns starting at first. */
+void oracle_act_bf16_range(uint32_t first, uint64_t count, int silu, uint16_t* out) {
+  for (uint64_t i = 0; i < count; ++i)
+    out[i] = oracle_act_bf16(float_of((uint32_t)(first + i)), silu);
+}
+
+/* oracle_act_bf16 over n FP32 bit patterns given in an array. */
+void oracle_act_bf16_list(const uint32_t* in, uint64_t n, int silu, uint16_t* out) {
+  for (uint64_t i = 0; i < n; ++i) out[i] = oracle_act_bf16(float_of(in[i]), silu);
+}
+
+/* The FP32 accumulator of one output: bias (or +0.0f), then one fused
+ * multiply-add per tap, oldest tap first. w points at the channel's four taps
+ * (stride ws1 between taps); hist holds e[t-3], e[t-2], e[t-1], cur is e[t]. */
+static float conv_acc(const float* w, int64_t ws1, const float* bias_c,
+                      const float hist[3], float cur) {
+  float acc = bias_c ? *bias_c : 0.0f;
+  acc = fmaf(w[0 * ws1], hist[0], acc);
+  acc = fmaf(w[1 * ws1], hist[1], acc);
+  acc = fmaf(w[2 * ws1], hist[2], acc);
+  acc = fmaf(w[3 * ws1], cur, acc);
+  return acc;
+}
+
+/* The whole operation on host arrays.
+ *
+ * x:           bf16 bits, row t / channel c at x[t * x_row_stride + c], t < num_tokens.
+ * weight:      FP32, tap k of channel c at weight[c * w_stride0 + k * w_stride1].
+ * bias:        FP32 (dim,) or NULL.
+ * conv_states: FP32, history k of channel c of line l at
+ *              conv_states[l * cs_stride0 + c * cs_stride1 + k * cs_stride2];
+ *              updated in place.
+ * query_start_loc: int32 (num_seqs + 1), sequence s owns rows [qsl[s], qsl[s+1]).
+ * cache_indices:   int32, the line of sequence s at cache_indices[s * ci_stride].
+ * has_initial_state: one byte per sequence, nonzero = start from the stored state;
+ *                    NULL = no sequence has one.
+ * out:         bf16 bits, dense (dim / part_dim, num_tokens, part_dim); rows no
+ *              sequence owns are left as they are.
+ * Returns ORACLE_EINVAL (and writes nothing) for shapes or metadata it cannot
+ * give a meaning to; ORACLE_OK otherwise. */
+int oracle_packed_causal_conv1d(
+    const uint16_t* x, int64_t num_tokens, int64_t dim, int64_t x_row_stride,
+    const float* weight, int64_t w_stride0, int64_t w_stride1, const float* bias,
+    float* conv_states, int64_t num_cache_lines, int64_t cs_stride0, int64_t cs_stride1,
+    int64_t cs_stride2, const int32_t* query_start_loc, int64_t num_seqs,
+    const int32_t* cache_indices, int64_t ci_stride, const uint8_t* has_initial_state,
+    int64_t part_dim, int silu, int has_null_block, int64_t null_block_id, uint16_t* out) {
+  if (num_tokens < 0 || dim < 0 || num_seqs < 0 || part_dim <= 0 || dim % part_dim != 0)
+    return ORACLE_EINVAL;
+  if (x_row_stride < dim) return ORACLE_EINVAL;
+  /* Metadata check first, so that a rejected call leaves every output alone. */
+  for (int64_t s = 0; s < num_seqs; ++s) {
+    int64_t start = query_start_loc[s], end = query_start_loc[s + 1];
+    if (start < 0 || end < start || end > num_tokens) return ORACLE_EINVAL;
+    int64_t line = cache_indices[s * ci_stride];
+    int live = !(has_null_block && line == null_block_id);
+    if (live && end > start && (line < 0 || line >= num_cache_lines)) return ORACLE_EINVAL;
+  }
+
+  for (int64_t s = 0; s < num_seqs; ++s) {
+    int64_t start = query_start_loc[s], end = query_start_loc[s + 1];
+    int64_t len = end - start;
+    if (len == 0) continue; /* nothing to convolve, state untouched */
+    int64_t line = cache_indices[s * ci_stride];
+    int live = !(has_null_block && line == null_block_id);
+    int init = live && has_initial_state && has_initial_state[s];
+    for (int64_t c = 0; c < dim; ++c) {
+      float hist[3] = {0.0f, 0.0f, 0.0f}; /* e[t-3], e[t-2], e[t-1] */
+      if (init)
+        for (int k = 0; k < 3; ++k)
+          hist[k] = conv_states[line * cs_stride0 + c * cs_stride1 + k * cs_stride2];
+      const float* w = weight + c * w_stride0;
+      const float* b = bias ? bias + c : NULL;
+      int64_t plane = c / part_dim, col = c % part_dim;
+      for (int64_t i = 0; i < len; ++i) {
+        int64_t t = start + i;
+        float cur = oracle_bf16_to_f32(x[t * x_row_stride + c]);
+        float acc = conv_acc(w, w_stride1, b, hist, cur);
+        out[(plane * num_tokens + t) * part_dim + col] = oracle_act_bf16(acc, silu);
+        hist[0] = hist[1];
+        hist[1] = hist[2];
+        hist[2] = cur;
+      }
+      /* The window now holds the last three values of (history ++ x). */
+      if (live)
+        for (int k = 0; k < 3; ++k)
+          conv_states[line * cs_stride0 + c * cs_stride1 + k * cs_stride2] = hist[k];
+    }
+  }
+  return ORACLE_OK;
+}
+
+/* Certificate scan for oracle_crexpf over the FP32 bit patterns [first, first+count):
+ * counts the inputs that take the quad branch and, among them, returns the
+ * smallest distance (relative to the value) between the quad result and the
+ * nearest binary32 midpoint, as a power-of-two exponent in *min_log2_gap.
+ * Inputs with an escalation are written to cand (up to cand_cap of them). */
+uint64_t oracle_crexpf_scan(uint32_t first, uint64_t count, uint32_t* cand, uint64_t cand_cap,
+                            double* min_log2_gap) {
+  uint64_t n = 0;
+  double worst = 0.0;
+  for (uint64_t i = 0; i < count; ++i) {
+    uint32_t u = (uint32_t)(first + i);
+    float x = float_of(u);
+    if (!oracle_crexpf_escalates(x)) continue;
+    if (n < cand_cap) cand[n] = u;
+    ++n;
+    __float128 q = expq((__float128)x);
+    double e = (double)q;
+    float r = (float)q;
+    float below = ((double)r > e) ? nextafterf(r, 0.0f) : r;
+    if (isinf(r)) below = 0x1.fffffep127f;
+    float up = nextafterf(below, INFINITY);
+    __float128 above = isinf(up) ? (__float128)0x1p128 : (__float128)up;
+    __float128 mid = ((__float128)below + above) / 2;
+    __float128 gap = (q - mid) / q;
+    if (gap < 0) gap = -gap;
+    double g = log2((double)gap);
+    if (n == 1 || g < worst) worst = g;
+  }
+  *min_log2_gap = worst;
+  return n;
+}

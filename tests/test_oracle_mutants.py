@@ -1,0 +1,88 @@
+"""Planted mistakes: the pins must catch a plausible bug anywhere in the oracle.
+
+Each case patches the oracle's C source in a temporary directory (the committed
+source is never touched), builds it with the same flags, and runs the pin tests
+against the mutant. A mutant that passes every pin is a hole in the pins.
+"""
+
+import pathlib
+
+import pytest
+
+import oracle
+import test_oracle_act as act_pins
+import test_oracle_conv as conv_pins
+import test_oracle_rounding as round_pins
+
+SRC = oracle.SOURCE.read_text()
+
+MUTANTS = {
+    "taps reversed": [("fmaf(w[0 * ws1], hist[0], acc)", "fmaf(w[0 * ws1], cur, acc)"),
+                      ("fmaf(w[3 * ws1], cur, acc)", "fmaf(w[3 * ws1], hist[0], acc)")],
+    "bias dropped": [("float acc = bias_c ? *bias_c : 0.0f;", "float acc = 0.0f;")],
+    "taps newest first": [("fmaf(w[0 * ws1], hist[0], acc);\n  acc = fmaf(w[1 * ws1], hist[1], acc);\n"
+                           "  acc = fmaf(w[2 * ws1], hist[2], acc);\n  acc = fmaf(w[3 * ws1], cur, acc);",
+                           "fmaf(w[3 * ws1], cur, acc);\n  acc = fmaf(w[2 * ws1], hist[2], acc);\n"
+                           "  acc = fmaf(w[1 * ws1], hist[1], acc);\n  acc = fmaf(w[0 * ws1], hist[0], acc);")],
+    "bias added last": [("float acc = bias_c ? *bias_c : 0.0f;", "float acc = 0.0f;"),
+                        ("acc = fmaf(w[3 * ws1], cur, acc);\n  return acc;",
+                         "acc = fmaf(w[3 * ws1], cur, acc);\n  return bias_c ? acc + *bias_c : acc;")],
+    "unfused multiply-add": [("acc = fmaf(w[1 * ws1], hist[1], acc);",
+                              "acc = w[1 * ws1] * hist[1] + acc;")],
+    "silu sign": [("oracle_crexpf(-a)", "oracle_crexpf(a)")],
+    "silu via reciprocal": [("y = a / d;", "y = a * (1.0f / d);")],
+    "state written newest first": [("k * cs_stride2] = hist[k];", "k * cs_stride2] = hist[2 - k];")],
+    "state never read": [("int init = live && has_initial_state && has_initial_state[s];",
+                          "int init = 0;")],
+    "null block ignored": [("int live = !(has_null_block && line == null_block_id);\n    int init",
+                            "int live = 1;\n    int init")],
+    "window shift wrong": [("hist[0] = hist[1];\n        hist[1] = hist[2];",
+                            "hist[1] = hist[2];\n        hist[0] = hist[1];")],
+    "planes transposed": [("out[(plane * num_tokens + t) * part_dim + col]",
+                           "out[(t * (dim / part_dim) + plane) * part_dim + col]")],
+    "ties away from even": [("(dropped == 0x8000u && (kept & 1u))", "(dropped == 0x8000u)")],
+    "bf16 truncates": [("if (dropped > 0x8000u || (dropped == 0x8000u && (kept & 1u))) kept += 1;",
+                        "(void)dropped;")],
+    "exp one ulp high": [("    return (float)q;\n  }\n  return (float)e;",
+                          "    return (float)q;\n  }\n  return nextafterf((float)e, INFINITY);")],
+}
+
+PINS = [
+    *[(f"brute force {s}", lambda lib, s=s: conv_pins.test_brute_force_exact(lib, s)) for s in range(6)],
+    *[(f"unit tap {t}", lambda lib, t=t: conv_pins.test_unit_taps_shift_the_input(lib, t)) for t in range(4)],
+    ("near midpoints", conv_pins.test_brute_force_near_bf16_midpoints),
+    ("bias first", conv_pins.test_bias_enters_first),
+    ("oldest first", conv_pins.test_taps_enter_oldest_first),
+    ("ones", lambda lib: conv_pins.test_all_ones_taps_sum_integers(lib, False)),
+    ("plane layout", conv_pins.test_plane_layout),
+    ("state last three", lambda lib: conv_pins.test_state_is_last_three_inputs(lib, True)),
+    ("null block", conv_pins.test_null_block_runs_from_zero_and_leaves_its_line),
+    ("torch conv1d silu", lambda lib: conv_pins.test_against_torch_conv1d_float64(lib, 0, True)),
+    ("silu random", act_pins.test_silu_random_against_exact),
+    ("silu near midpoints", act_pins.test_silu_near_bf16_midpoints),
+    ("bf16 closed forms", lambda lib: [round_pins.test_bf16_round_closed_forms(lib, u)
+                                       for u in (0x3F808000, 0x3F818000, 0x00018000)]),
+]
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(name, tmp_path: pathlib.Path):
+    src = SRC
+    for old, new in MUTANTS[name]:
+        assert src.count(old) == 1, f"patch for {name!r} no longer matches the oracle source"
+        src = src.replace(old, new)
+    mutant_src = tmp_path / "kdaconv_oracle.c"
+    mutant_src.write_text(src)
+    so = tmp_path / "libmutant.so"
+    import subprocess
+
+    subprocess.run(["gcc", *oracle._CFLAGS, "-o", str(so), str(mutant_src), "-lquadmath", "-lm"],
+                   check=True)
+    lib = oracle.load(so)
+    caught = []
+    for pin_name, pin in PINS:
+        try:
+            pin(lib)
+        except (AssertionError, ValueError):
+            caught.append(pin_name)
+    assert caught, f"no pin catches the planted mistake {name!r}"

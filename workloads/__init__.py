@@ -1,0 +1,259 @@
+"""Seeded synthetic inputs for the packed varlen causal depthwise convolution.
+
+This module only draws inputs. It holds none of the convolution's arithmetic and
+is shared by the tests, the bench and the smoke check, which hand the same arrays
+both to the CPU oracle and to the HIP path.
+
+Every array comes from ``numpy.random.Generator(PCG64(seed))`` in a fixed order
+of draws, so a (config, seed) pair gives the same bytes on every host. Float
+inputs are drawn as float32 and rounded to bfloat16 (round to nearest even) by
+the helper below, which is input preparation, not the method.
+
+Shapes follow the workloads the kda_conv page talks about (vllm.models.kimi_k3.
+nvidia.ops.kda_conv, the ``_config`` comment: 2K-16K tokens x 3 x 1536 packed
+Q|K|V channels read in place from the in_proj output) and the five named
+configurations listed in ``CONFIGS``.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+
+#: bf16 quiet NaN written into the x columns the op must never read (canary).
+BF16_CANARY = 0x7FC0
+
+#: Row stride (elements) of the in_proj output the Q|K|V columns live in.
+IN_PROJ_ROW_STRIDE = 9728
+
+
+@dataclasses.dataclass
+class Workload:
+    """One call's worth of host inputs.
+
+    ``x`` is the whole row-strided bf16 buffer, shape ``(num_tokens, row_stride)``,
+    stored as raw uint16 bit patterns; the op reads its first ``dim`` columns.
+    """
+
+    name: str
+    x: np.ndarray  # uint16 (T, row_stride)
+    dim: int
+    weight: np.ndarray  # float32 (dim, 4) [channel, tap]
+    bias: Optional[np.ndarray]  # float32 (dim,) or None
+    conv_states: np.ndarray  # float32 (lines, dim, 3)
+    query_start_loc: np.ndarray  # int32 (S + 1,)
+    cache_indices: np.ndarray  # int32 (S,)
+    has_initial_state: np.ndarray  # bool (S,)
+    part_dim: int
+    activation: Optional[str]  # "silu" or None
+    null_block_id: Optional[int]
+
+    @property
+    def num_tokens(self) -> int:
+        return int(self.x.shape[0])
+
+    @property
+    def num_seqs(self) -> int:
+        return int(self.query_start_loc.shape[0]) - 1
+
+    @property
+    def row_stride(self) -> int:
+        return int(self.x.shape[1])
+
+    @property
+    def num_cache_lines(self) -> int:
+        return int(self.conv_states.shape[0])
+
+    def algorithmic_bytes(self) -> int:
+        """Bytes the operation must move (no halo re-reads, no slack work).
+
+        x read and out written once (2 B each per element), 12 B of state per
+        channel read for every sequence that starts from its stored state and
+        written for every live non-empty sequence, the weight (16 B per channel),
+        the bias (4 B per channel) and the per-sequence metadata.
+        """
+        qsl = self.query_start_loc.astype(np.int64)
+        lens = qsl[1:] - qsl[:-1]
+        live = np.ones(self.num_seqs, dtype=bool)
+        if self.null_block_id is not None:
+            live &= self.cache_indices != self.null_block_id
+        reads_state = live & self.has_initial_state
+        writes_state = live & (lens > 0)
+        tokens = int(qsl[-1]) if self.num_seqs > 0 else 0
+        b = tokens * self.dim * 2 * 2
+        b += 12 * self.dim * int(reads_state.sum())
+        b += 12 * self.dim * int(writes_state.sum())
+        b += 16 * self.dim
+        if self.bias is not None:
+            b += 4 * self.dim
+        b += 4 * (self.num_seqs + 1) + 4 * self.num_seqs + self.num_seqs
+        return b
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round finite float32 values to bfloat16 bit patterns (nearest, ties to even)."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    r = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
+    return ((u + r) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(h: np.ndarray) -> np.ndarray:
+    """Widen bfloat16 bit patterns to float32 (exact)."""
+    return (np.asarray(h, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _x_buffer(rng: np.random.Generator, tokens: int, dim: int, row_stride: int,
+              scale: float = 1.0) -> np.ndarray:
+    vals = rng.standard_normal((tokens, dim), dtype=np.float32)
+    if scale != 1.0:
+        vals *= np.float32(scale)
+    x = np.full((tokens, row_stride), BF16_CANARY, dtype=np.uint16)
+    x[:, :dim] = f32_to_bf16_bits(vals)
+    return x
+
+
+def _normal(rng: np.random.Generator, shape, sigma: float) -> np.ndarray:
+    return (rng.standard_normal(shape, dtype=np.float32) * np.float32(sigma)).astype(np.float32)
+
+
+def _qsl(lengths: np.ndarray) -> np.ndarray:
+    q = np.zeros(len(lengths) + 1, dtype=np.int64)
+    np.cumsum(lengths, out=q[1:])
+    return q.astype(np.int32)
+
+
+def config1(seed: int = 1) -> Workload:
+    """1 sequence of 64 tokens, dim 384 as 3 planes of 128, contiguous x, zero state, no init."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    T, dim = 64, 384
+    x = _x_buffer(rng, T, dim, dim)
+    w = _normal(rng, (dim, 4), 0.5)
+    b = _normal(rng, (dim,), 0.1)
+    st = np.zeros((1, dim, 3), dtype=np.float32)
+    return Workload("config1: 1 x 64 tokens, dim 384, part_dim 128", x, dim, w, b, st,
+                    _qsl(np.array([T])), np.array([0], dtype=np.int32),
+                    np.array([False]), 128, "silu", None)
+
+
+def config2(seed: int = 2) -> Workload:
+    """8 sequences of 1-300 tokens, dim 4608 (3 x 1536) in rows of 9728, 4 with initial state."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    dim, S, lines = 4608, 8, 64
+    lens = rng.integers(1, 300, size=S, endpoint=True)
+    T = int(lens.sum())
+    x = _x_buffer(rng, T, dim, IN_PROJ_ROW_STRIDE)
+    w = _normal(rng, (dim, 4), 0.5)
+    b = _normal(rng, (dim,), 0.1)
+    st = _normal(rng, (lines, dim, 3), 1.0)
+    ci = rng.permutation(lines)[:S].astype(np.int32)
+    init = np.zeros(S, dtype=bool)
+    init[rng.choice(S, size=4, replace=False)] = True
+    return Workload("config2: 8 seqs of 1-300 tokens, dim 4608, part_dim 1536, stride 9728",
+                    x, dim, w, b, st, _qsl(lens), ci, init, 1536, "silu", None)
+
+
+def config3(seed: int = 3) -> Workload:
+    """1 sequence of 16384 tokens, dim 4608 (3 x 1536) in rows of 9728, initial state."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    T, dim, lines = 16384, 4608, 8
+    x = _x_buffer(rng, T, dim, IN_PROJ_ROW_STRIDE)
+    w = _normal(rng, (dim, 4), 0.5)
+    b = _normal(rng, (dim,), 0.1)
+    st = _normal(rng, (lines, dim, 3), 1.0)
+    ci = np.array([rng.integers(lines)], dtype=np.int32)
+    return Workload("config3: 1 x 16384 tokens, dim 4608, part_dim 1536, stride 9728",
+                    x, dim, w, b, st, _qsl(np.array([T])), ci, np.array([True]), 1536,
+                    "silu", None)
+
+
+def lognormal_lengths(rng: np.random.Generator, count: int, total: int,
+                      sigma: float = 1.0) -> np.ndarray:
+    """``count`` lengths >= 1 summing to ``total``: log-normal shares, largest remainder."""
+    raw = rng.lognormal(mean=0.0, sigma=sigma, size=count)
+    spare = total - count
+    share = raw / raw.sum() * spare
+    base = np.floor(share).astype(np.int64)
+    rem = spare - int(base.sum())
+    order = np.argsort(-(share - base), kind="stable")
+    base[order[:rem]] += 1
+    return base + 1
+
+
+def config4(seed: int = 4) -> Workload:
+    """64 sequences, log-normal lengths plus 1, 2, 3 (16384 tokens), a null-block sequence."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    dim, S, lines, T = 4608, 64, 256, 16384
+    lens = np.concatenate([lognormal_lengths(rng, S - 3, T - 6), np.array([1, 2, 3])])
+    lens = lens[rng.permutation(S)]
+    x = _x_buffer(rng, T, dim, IN_PROJ_ROW_STRIDE)
+    w = _normal(rng, (dim, 4), 0.5)
+    b = _normal(rng, (dim,), 0.1)
+    st = _normal(rng, (lines, dim, 3), 1.0)
+    null_seq = int(rng.integers(S))
+    others = (rng.permutation(lines - 1)[: S - 1] + 1).astype(np.int32)
+    ci = np.empty(S, dtype=np.int32)
+    ci[null_seq] = 0
+    ci[np.arange(S) != null_seq] = others
+    init = np.zeros(S, dtype=bool)
+    init[rng.choice(S, size=48, replace=False)] = True
+    return Workload("config4: 64 log-normal seqs (16384 tokens), null block 0, stride 9728",
+                    x, dim, w, b, st, _qsl(lens), ci, init, 1536, "silu", 0)
+
+
+def config5(seed: int = 5) -> Workload:
+    """4096 sequences of 1-4 tokens, dim 576 as 3 planes of 192, no bias, no activation."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    dim, S, lines = 576, 4096, 8192
+    lens = rng.integers(1, 4, size=S, endpoint=True)
+    T = int(lens.sum())
+    x = _x_buffer(rng, T, dim, dim)
+    w = _normal(rng, (dim, 4), 0.5)
+    st = _normal(rng, (lines, dim, 3), 1.0)
+    ci = rng.permutation(lines)[:S].astype(np.int32)
+    init = np.ones(S, dtype=bool)
+    return Workload("config5: 4096 seqs of 1-4 tokens, dim 576, part_dim 192, no bias, no act",
+                    x, dim, w, None, st, _qsl(lens), ci, init, 192, None, None)
+
+
+CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}
+
+
+def random_case(seed: int, *, max_seqs: int = 12, max_len: int = 200, parts: int = 3,
+                part_dim: Optional[int] = None, x_scale: float = 1.0,
+                allow_empty: bool = True, pad_tokens: int = 0,
+                row_pad: Optional[int] = None) -> Workload:
+    """Random fuzz case: zero-length sequences, null block, strides, padding rows.
+
+    ``x_scale`` widens the accumulator range so that large negative and positive
+    SiLU arguments appear; ``pad_tokens`` appends rows after the last sequence
+    that no sequence owns.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    S = int(rng.integers(1, max_seqs, endpoint=True))
+    lo = 0 if allow_empty else 1
+    lens = rng.integers(lo, max_len, size=S, endpoint=True)
+    if allow_empty and S > 1:
+        lens[rng.random(S) < 0.2] = 0
+    if part_dim is None:
+        part_dim = int(rng.choice([8, 16, 64, 72, 128, 192, 256, 520]))
+    dim = parts * part_dim
+    if row_pad is None:
+        row_pad = int(rng.choice([0, 8, 64, 5136]))
+    row_stride = dim + row_pad
+    T = int(lens.sum()) + pad_tokens
+    x = _x_buffer(rng, T, dim, row_stride, x_scale)
+    w = _normal(rng, (dim, 4), 0.5)
+    has_bias = bool(rng.integers(2))
+    b = _normal(rng, (dim,), 0.1) if has_bias else None
+    lines = S + int(rng.integers(1, 5))
+    st = _normal(rng, (lines, dim, 3), float(x_scale))
+    ci = rng.permutation(lines)[:S].astype(np.int32)
+    init = rng.random(S) < 0.6
+    null_id = None
+    if bool(rng.integers(2)):
+        null_id = int(ci[int(rng.integers(S))])
+    act = "silu" if bool(rng.integers(4)) else None
+    return Workload(f"random seed {seed}: S={S} dim={dim} pd={part_dim} stride={row_stride}",
+                    x, dim, w, b, st, _qsl(lens), ci, init, part_dim, act, null_id)
