@@ -1,0 +1,193 @@
+"""Packed varlen causal depthwise width-4 convolution (KDA prefill short conv) on MI355X.
+
+Python face of libkdaconv (include/kdaconv.h): the two functions of the page
+"vllm.models.kimi_k3.nvidia.ops.kda_conv", ``packed_causal_conv1d_fn`` and
+``packed_causal_conv1d_supported``, with the same arguments. PyTorch supplies the
+device memory and the current stream; every step of the computation runs in the
+HIP kernels of libkdaconv. There is no CPU path: if the library is not built,
+importing the functions still works but calling them raises.
+"""
+
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import _lib
+
+__all__ = [
+    "NULL_BLOCK_ID",
+    "packed_causal_conv1d_fn",
+    "packed_causal_conv1d_supported",
+    "activation_map",
+    "library_path",
+]
+
+#: Default null block id. The page names the default (NULL_BLOCK_ID) without
+#: printing its value; 0, the block the paged cache reserves as its null block,
+#: is taken here. Pass the id explicitly (or None) to be independent of this.
+NULL_BLOCK_ID = 0
+
+
+def library_path() -> str:
+    return str(_lib.LIBRARY)
+
+
+def _activation_code(activation) -> int:
+    # The page selects SiLU for "silu", "swish" or True; identity for None or False.
+    if activation in ("silu", "swish", True):
+        return _lib.ACT_SILU
+    if activation is None or activation is False:
+        return _lib.ACT_NONE
+    raise ValueError(f"unknown activation {activation!r}: use 'silu', 'swish', True, None or False")
+
+
+def _stream_handle(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _conv_args(x, weight, bias, conv_states, query_start_loc, cache_indices, has_initial_state,
+               part_dim, activation, null_block_id, out):
+    num_tokens, dim = x.shape
+    num_seqs = query_start_loc.numel() - 1
+    return [
+        _ptr(x), num_tokens, dim, x.stride(0),
+        _ptr(weight), weight.stride(0), weight.stride(1), _ptr(bias),
+        _ptr(conv_states), conv_states.size(0),
+        conv_states.stride(0), conv_states.stride(1), conv_states.stride(2),
+        _ptr(query_start_loc), num_seqs,
+        _ptr(cache_indices), cache_indices.stride(0) if cache_indices.dim() == 1 else 0,
+        _ptr(has_initial_state),
+        int(part_dim), _activation_code(activation),
+        int(null_block_id is not None), 0 if null_block_id is None else int(null_block_id),
+        _ptr(out),
+    ]
+
+
+def _check_tensors(x, weight, bias, conv_states, query_start_loc, cache_indices, has_initial_state):
+    if not x.is_cuda:
+        raise ValueError("x must be a GPU tensor")
+    if x.dtype != torch.bfloat16:
+        raise ValueError(f"x must be bfloat16 (got {x.dtype})")
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D (tokens, dim) with unit column stride")
+    dim = x.size(1)
+    if weight.dtype != torch.float32 or weight.dim() != 2 or tuple(weight.shape) != (dim, 4):
+        raise ValueError("weight must be float32 of shape (dim, 4)")
+    if bias is not None and (bias.dtype != torch.float32 or tuple(bias.shape) != (dim,)
+                             or not bias.is_contiguous()):
+        raise ValueError("bias must be a contiguous float32 (dim,) tensor or None")
+    if conv_states.dtype != torch.float32 or conv_states.dim() != 3 or conv_states.size(1) != dim:
+        raise ValueError("conv_states must be float32 of shape (cache lines, dim, 3)")
+    if conv_states.size(2) != 3:
+        raise ValueError("conv_states must have exactly 3 history entries per channel")
+    if query_start_loc.dtype != torch.int32 or query_start_loc.dim() != 1:
+        raise ValueError("query_start_loc must be a 1-D int32 tensor")
+    if not query_start_loc.is_contiguous():
+        raise ValueError("query_start_loc must be contiguous")
+    num_seqs = query_start_loc.numel() - 1
+    if cache_indices.dtype != torch.int32 or cache_indices.dim() != 1 or cache_indices.numel() < num_seqs:
+        raise ValueError("cache_indices must be a 1-D int32 tensor with one entry per sequence")
+    if has_initial_state is not None:
+        if has_initial_state.dtype not in (torch.bool, torch.uint8) or not has_initial_state.is_contiguous():
+            raise ValueError("has_initial_state must be a contiguous bool tensor or None")
+        if has_initial_state.numel() < num_seqs:
+            raise ValueError("has_initial_state needs one entry per sequence")
+    for t in (weight, bias, conv_states, query_start_loc, cache_indices, has_initial_state):
+        if t is not None and t.device != x.device:
+            raise ValueError("all tensors must be on the device of x")
+
+
+def packed_causal_conv1d_fn(
+    x: torch.Tensor,
+    weight: torch.Tensor,
+    bias: Optional[torch.Tensor],
+    conv_states: torch.Tensor,
+    query_start_loc: torch.Tensor,
+    cache_indices: torch.Tensor,
+    has_initial_state: Optional[torch.Tensor],
+    part_dim: int,
+    activation="silu",
+    null_block_id: Optional[int] = NULL_BLOCK_ID,
+    out: Optional[torch.Tensor] = None,
+) -> torch.Tensor:
+    """Varlen causal depthwise width-4 conv of x (tokens, dim), dim = parts x part_dim.
+
+    Semantics of page vllm.models.kimi_k3.nvidia.ops.kda_conv,
+    packed_causal_conv1d_fn: causal_conv1d_fn(x.T, weight, bias, conv_states, ...).T
+    with conv_states (cache lines, dim, 3) updated in place. Returns
+    (dim // part_dim, tokens, part_dim) bf16; plane i holds channels
+    [i * part_dim, (i + 1) * part_dim). ``out``, when given, must be a contiguous
+    bf16 tensor of that shape and receives the result (rows no sequence owns are
+    left as they were). Queued on the current stream; no synchronisation.
+    """
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D (tokens, dim)")
+    num_tokens, dim = x.shape
+    if part_dim <= 0 or dim % part_dim != 0:
+        raise ValueError(f"dim {dim} is not a multiple of part_dim {part_dim}")
+    shape = (dim // part_dim, num_tokens, part_dim)
+    if out is None:
+        out = torch.empty(shape, dtype=x.dtype, device=x.device)
+    elif tuple(out.shape) != shape or out.dtype != x.dtype or not out.is_contiguous() or out.device != x.device:
+        raise ValueError(f"out must be a contiguous {x.dtype} tensor of shape {shape} on {x.device}")
+    # Nothing to convolve: return before touching anything (page: early return).
+    if num_tokens == 0 or query_start_loc.numel() <= 1:
+        return out
+    _check_tensors(x, weight, bias, conv_states, query_start_loc, cache_indices, has_initial_state)
+    lib = _lib.load()
+    args = _conv_args(x, weight, bias, conv_states, query_start_loc, cache_indices,
+                      has_initial_state, part_dim, activation, null_block_id, out)
+    with torch.cuda.device(x.device):
+        rc = lib.kdaconv_packed_causal_conv1d(*args, _stream_handle(x.device))
+    _lib.check(rc, "packed_causal_conv1d_fn")
+    return out
+
+
+def packed_causal_conv1d_supported(x: torch.Tensor, weight: torch.Tensor,
+                                   conv_states: torch.Tensor, part_dim: int) -> bool:
+    """Whether packed_causal_conv1d_fn serves these tensors (page:
+    packed_causal_conv1d_supported). This build takes bf16 x with unit column
+    stride and a row stride that is a multiple of 8, FP32 weight (dim, 4), FP32
+    conv_states (lines, dim, 3), and part_dim a multiple of 8 dividing dim."""
+    try:
+        if not (x.is_cuda and x.dim() == 2 and x.stride(1) == 1 and x.dtype == torch.bfloat16):
+            return False
+        if not (weight.dtype == torch.float32 and weight.dim() == 2
+                and tuple(weight.shape) == (x.size(1), 4)):
+            return False
+        if not (conv_states.dtype == torch.float32 and conv_states.dim() == 3
+                and conv_states.size(1) == x.size(1) and conv_states.size(2) == 3):
+            return False
+        if part_dim <= 0 or x.size(1) % part_dim != 0:
+            return False
+        lib = _lib.load()
+    except _lib.LibraryMissing:
+        return False
+    num_tokens, dim = x.shape
+    # The output buffer would be a fresh 256-byte-aligned allocation.
+    rc = lib.kdaconv_validate(
+        _ptr(x), num_tokens, dim, x.stride(0), _ptr(weight), weight.stride(0), weight.stride(1),
+        None, _ptr(conv_states), conv_states.size(0), conv_states.stride(0),
+        conv_states.stride(1), conv_states.stride(2), 256, 1, 256, 1, None, int(part_dim),
+        _lib.ACT_SILU, 0, 0, 256)
+    return rc == _lib.OK
+
+
+def activation_map(first: int, count: int, activation, out: Optional[torch.Tensor] = None
+                   ) -> torch.Tensor:
+    """The kernel's FP32 -> stored-bf16-word map on ``count`` consecutive FP32 bit
+    patterns from ``first``; returns an int16 tensor of words on the current device."""
+    if out is None:
+        out = torch.empty(count, dtype=torch.int16, device="cuda")
+    lib = _lib.load()
+    with torch.cuda.device(out.device):
+        rc = lib.kdaconv_activation_map(first & 0xFFFFFFFF, count, _activation_code(activation),
+                                        out.data_ptr(), _stream_handle(out.device))
+    _lib.check(rc, "activation_map")
+    return out

@@ -1,0 +1,470 @@
+// libkdaconv: packed varlen causal depthwise width-4 convolution for MI355X (gfx950).
+//
+// Page "vllm.models.kimi_k3.nvidia.ops.kda_conv" (module docstring; the
+// packed_causal_conv1d_fn docstring and source; packed_causal_conv1d_supported)
+// defines the operation; include/kdaconv.h states it in full.
+//
+// Work decomposition. A program is one wave64 handling one token chunk of one
+// sequence over 64 * kLaneChannels channels: each lane owns 4 consecutive
+// channels (an 8-byte bf16 vector), so every x row and every output row moves as
+// one vector per lane, 512 contiguous bytes per wave. Programs are
+// numbered so that sequence s owns programs v(s) .. v(s+1)-1 with
+// v(s) = s + floor(qsl[s] / kChunk); the wave finds its sequence on the device
+// with a radix-64 search over query_start_loc (one ballot per level), so the
+// grid, cdiv(T, kChunk) + num_seqs programs by the column blocks, depends only
+// on host sizes and the launch can be captured in a graph. Chunk j of sequence
+// s covers rows [start + j*kChunk, start + (j+1)*kChunk) of the sequence;
+// programs past the end of their sequence exit at once.
+//
+// Streaming. x, out and the state line are addressed through buffer
+// descriptors whose base is the program's first row: the lane's channel offset
+// is a fixed vector register and each row's offset a scalar, so no per-row
+// vector address arithmetic runs. A lane keeps the 3 history rows of its
+// channels in registers and a queue of kDepth rows in flight: consuming row r
+// refills its slot with row r + kDepth. Lanes past the launch's last channel
+// (only in a partial last column block) load a valid channel and store nothing.
+//
+// State. Only the first chunk of a sequence reads the sequence's conv-state
+// line, and the same program writes the updated line after its reads (page,
+// module docstring).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "kdaconv.h"
+#include "kdaconv_device.h"
+
+namespace kdaconv {
+namespace {
+
+constexpr int kWave = 64;
+constexpr int kChunk = 64;  // tokens per program
+constexpr int kDepth = 8;  // rows in flight per lane
+constexpr int kMinWaves = 4;  // occupancy target: at most 128 VGPRs
+constexpr int kLaneChannels = 4;  // channels per lane (8-byte vectors)
+constexpr uint32_t kDescWord3 = 0x00020000u;  // gfx9 raw buffer: 32-bit data format
+constexpr int32_t kRange = 0x7FFFFFFF;
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <int V>
+struct Lane;
+
+template <>
+struct Lane<4> {
+  typedef u32x2 vec;
+  static __device__ __forceinline__ vec load(__amdgpu_buffer_rsrc_t r, uint32_t vo, uint32_t so) {
+    return __builtin_amdgcn_raw_buffer_load_b64(r, vo, so, 0);
+  }
+  static __device__ __forceinline__ void store(vec v, __amdgpu_buffer_rsrc_t r, uint32_t vo,
+                                               uint32_t so) {
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, vo, so, 0);
+  }
+};
+
+struct ConvParams {
+  const uint16_t* x;
+  const float* weight;
+  const float* bias;
+  float* states;
+  const int32_t* __restrict__ qsl;
+  const int32_t* __restrict__ cache_indices;
+  const uint8_t* __restrict__ has_init;
+  uint16_t* out;  // first plane of this launch
+  int64_t x_row_stride;
+  int64_t w_stride0, w_stride1;
+  int64_t cs_stride0, cs_stride1, cs_stride2;
+  int64_t ci_stride;
+  int64_t num_cache_lines;
+  int64_t plane_stride;  // num_tokens * part_dim
+  int64_t null_block_id;
+  int32_t num_tokens;
+  int32_t num_seqs;
+  int32_t col_begin;  // first channel of this launch
+  int32_t col_end;  // one past its last channel
+  int32_t part_dim;
+  int32_t search_levels;  // radix-64 levels: smallest L with 64^L >= num_seqs
+  int32_t search_top;  // 64^(search_levels - 1)
+  int32_t has_null_block;
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, kRange, kDescWord3);
+}
+
+template <int V>
+__device__ __forceinline__ void unpack(typename Lane<V>::vec v, float (&f)[V]) {
+#pragma unroll
+  for (int i = 0; i < V / 2; ++i) {
+    f[2 * i] = widen_lo(v[i]);
+    f[2 * i + 1] = widen_hi(v[i]);
+  }
+}
+
+template <bool kSilu, int V>
+__device__ __forceinline__ typename Lane<V>::vec activate(const float (&acc)[V]) {
+  uint32_t u[V / 2];
+  activate_words<kSilu, V>(acc, u);
+  typename Lane<V>::vec w;
+#pragma unroll
+  for (int i = 0; i < V / 2; ++i) w[i] = u[i];
+  return w;
+}
+
+// Largest s in [0, num_seqs) with s + floor(qsl[s] / kChunk) <= p, or -1.
+// v(s) is strictly increasing for a non-decreasing qsl, so at each level the
+// lanes whose candidate passes form a prefix of the wave.
+__device__ __forceinline__ int find_sequence(const ConvParams& P, int p, int lane) {
+  int base = 0;
+  int stride = P.search_top;
+  for (int level = 0; level < P.search_levels; ++level) {
+    const int idx = base + lane * stride;
+    bool ok = false;
+    if (idx < P.num_seqs) {
+      const int q = max(P.qsl[idx], 0);
+      ok = idx + q / kChunk <= p;
+    }
+    const uint64_t m = __ballot(ok);
+    const int cnt = __popcll(m);
+    if (cnt == 0) return -1;
+    base += (cnt - 1) * stride;
+    stride /= kWave;
+  }
+  if (P.search_levels == 0 && max(P.qsl[0], 0) / kChunk > p) return -1;
+  return base;
+}
+
+template <int V, bool kBias, bool kSilu>
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(kMinWaves))) void packed_conv_kernel(const ConvParams P) {
+  typedef Lane<V> L;
+  typedef typename L::vec vec;
+  const int lane = threadIdx.x;
+  const int c0 = P.col_begin + (int)(blockIdx.y * kWave + lane) * V;
+  const bool active = c0 < P.col_end;
+  const int cl = active ? c0 : P.col_begin;  // inactive lanes compute on a valid channel
+
+  // Weights and bias first: their addresses do not depend on the search.
+  float w0[V], w1[V], w2[V], w3[V], bs[V];
+#pragma unroll
+  for (int k = 0; k < V; ++k) {
+    const float* wp = P.weight + (int64_t)(cl + k) * P.w_stride0;
+    w0[k] = wp[0];
+    w1[k] = wp[P.w_stride1];
+    w2[k] = wp[2 * P.w_stride1];
+    w3[k] = wp[3 * P.w_stride1];
+    bs[k] = kBias ? P.bias[cl + k] : 0.0f;
+  }
+
+  const int p = blockIdx.x;
+  const int s = find_sequence(P, p, lane);
+  if (s < 0) return;
+  const int T = P.num_tokens;
+  const int start = min(max(P.qsl[s], 0), T);
+  const int end = min(max(P.qsl[s + 1], start), T);
+  const int len = end - start;
+  const int j = p - (s + start / kChunk);
+  if ((int64_t)j * kChunk >= len) return;  // past the end of its sequence
+  const int t0 = start + j * kChunk;
+  const int n = min(kChunk, end - t0);
+
+  // x descriptor based at row t0 - 3 (later chunks read 3 history rows) or t0.
+  const int halo = j > 0 ? 3 : 0;
+  const uint32_t xrow_bytes = (uint32_t)(P.x_row_stride * 2);
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(P.x + (int64_t)(t0 - halo) * P.x_row_stride);
+  const uint32_t xvo = (uint32_t)(cl * 2);
+
+  // out descriptor based at row t0 of the launch's first plane; the lane's
+  // plane and column go into its fixed offset.
+  const int plane = (cl - P.col_begin) / P.part_dim;
+  const int col = (cl - P.col_begin) - plane * P.part_dim;
+  const uint32_t orow_bytes = (uint32_t)(P.part_dim * 2);
+  const __amdgpu_buffer_rsrc_t orsrc = make_rsrc(P.out + (int64_t)t0 * P.part_dim);
+  const uint32_t ovo = (uint32_t)((plane * P.plane_stride + col) * 2);
+
+  // Queue: rows 0 .. kDepth-1 of the chunk.
+  vec q[kDepth];
+#pragma unroll
+  for (int r = 0; r < kDepth; ++r)
+    if (r < n) q[r] = L::load(xr, xvo, (uint32_t)(r + halo) * xrow_bytes);
+
+  // History e[t0-3], e[t0-2], e[t0-1].
+  float h0[V], h1[V], h2[V];
+  bool live = false;
+  int64_t line = 0;
+  if (j == 0) {
+    line = P.cache_indices[(int64_t)s * P.ci_stride];
+    live = !(P.has_null_block && line == P.null_block_id) && line >= 0 &&
+           line < P.num_cache_lines;
+    const bool init = live && P.has_init != nullptr && P.has_init[s] != 0;
+    if (init) {
+      const float* sp = P.states + line * P.cs_stride0;
+#pragma unroll
+      for (int k = 0; k < V; ++k) {
+        const float* cp = sp + (int64_t)(cl + k) * P.cs_stride1;
+        h0[k] = cp[0];
+        h1[k] = cp[P.cs_stride2];
+        h2[k] = cp[2 * P.cs_stride2];
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < V; ++k) h0[k] = h1[k] = h2[k] = 0.0f;
+    }
+  } else {
+    unpack<V>(L::load(xr, xvo, 0), h0);
+    unpack<V>(L::load(xr, xvo, xrow_bytes), h1);
+    unpack<V>(L::load(xr, xvo, 2 * xrow_bytes), h2);
+  }
+
+  // One output row from the widened input row and the history; shifts the history.
+  auto step = [&](vec v, int row) {
+    float xv[V], acc[V];
+    unpack<V>(v, xv);
+#pragma unroll
+    for (int k = 0; k < V; ++k) {
+      float a = bs[k];
+      a = __builtin_fmaf(w0[k], h0[k], a);
+      a = __builtin_fmaf(w1[k], h1[k], a);
+      a = __builtin_fmaf(w2[k], h2[k], a);
+      a = __builtin_fmaf(w3[k], xv[k], a);
+      acc[k] = a;
+    }
+    const vec o = activate<kSilu, V>(acc);
+    if (active) L::store(o, orsrc, ovo, (uint32_t)row * orow_bytes);
+#pragma unroll
+    for (int k = 0; k < V; ++k) {
+      h0[k] = h1[k];
+      h1[k] = h2[k];
+      h2[k] = xv[k];
+    }
+  };
+
+  int done = 0;  // rows consumed; the queue holds rows done .. done + kDepth - 1
+  // Steady state: every consumed slot is refilled with a row that exists.
+  while (n - done >= 2 * kDepth) {
+#pragma unroll
+    for (int r = 0; r < kDepth; ++r) {
+      const vec v = q[r];
+      q[r] = L::load(xr, xvo, (uint32_t)(done + kDepth + r + halo) * xrow_bytes);
+      step(v, done + r);
+    }
+    done += kDepth;
+  }
+  // Drain: fewer than 2 * kDepth rows remain.
+#pragma unroll
+  for (int r = 0; r < kDepth; ++r) {
+    if (done + r < n) {
+      const vec v = q[r];
+      if (done + kDepth + r < n)
+        q[r] = L::load(xr, xvo, (uint32_t)(done + kDepth + r + halo) * xrow_bytes);
+      step(v, done + r);
+    }
+  }
+  done += kDepth;
+#pragma unroll
+  for (int r = 0; r < kDepth; ++r)
+    if (done + r < n) step(q[r], done + r);
+
+  // Updated state: the last three values of (history ++ x) for this sequence.
+  if (j == 0 && live && active) {
+    if (t0 + n < end) {
+      // The sequence continues past this chunk: its last rows are end-3 .. end-1.
+      const __amdgpu_buffer_rsrc_t tr = make_rsrc(P.x + (int64_t)(end - 3) * P.x_row_stride);
+      unpack<V>(L::load(tr, xvo, 0), h0);
+      unpack<V>(L::load(tr, xvo, xrow_bytes), h1);
+      unpack<V>(L::load(tr, xvo, 2 * xrow_bytes), h2);
+    }
+    float* sp = P.states + line * P.cs_stride0;
+#pragma unroll
+    for (int k = 0; k < V; ++k) {
+      float* cp = sp + (int64_t)(cl + k) * P.cs_stride1;
+      cp[0] = h0[k];
+      cp[P.cs_stride2] = h1[k];
+      cp[2 * P.cs_stride2] = h2[k];
+    }
+  }
+}
+
+// The activation map on consecutive FP32 bit patterns, 8 per thread, through
+// the same activate_words the convolution uses.
+template <bool kSilu>
+__global__ __launch_bounds__(256) void activation_map_kernel(uint32_t first, uint64_t count,
+                                                             uint16_t* __restrict__ out) {
+  const uint64_t i = ((uint64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  if (i >= count) return;
+  float acc[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) acc[k] = __uint_as_float(first + (uint32_t)(i + k));
+  uint32_t w[4];
+  activate_words<kSilu, 8>(acc, w);
+  *reinterpret_cast<uint4*>(out + i) = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int validate(const void* x, int64_t num_tokens, int64_t dim, int64_t x_row_stride,
+             const float* weight, int64_t ws0, int64_t ws1, const float* conv_states,
+             int64_t num_cache_lines, int64_t cs0, int64_t cs1, int64_t cs2, const int32_t* qsl,
+             int64_t num_seqs, const int32_t* ci, int64_t ci_stride, int64_t part_dim,
+             int activation, const void* out) {
+  if (num_tokens < 0 || dim < 0 || num_seqs < 0 || num_cache_lines < 0) return KDACONV_EINVAL;
+  if (part_dim <= 0 || dim % part_dim != 0) return KDACONV_EINVAL;
+  if (x_row_stride < dim) return KDACONV_EINVAL;
+  if (activation != KDACONV_ACT_NONE && activation != KDACONV_ACT_SILU) return KDACONV_EINVAL;
+  if (part_dim % 8 != 0 || x_row_stride % 8 != 0) return KDACONV_EUNSUPPORTED;
+  if (ws0 < 0 || ws1 < 0 || cs0 < 0 || cs1 < 0 || cs2 < 0 || ci_stride < 0)
+    return KDACONV_EUNSUPPORTED;
+  // int32 token and sequence indices; 32-bit offsets within a program's rows
+  // and within one output plane.
+  if (num_tokens > INT32_MAX - 1 || num_seqs > INT32_MAX / 2 || dim > INT32_MAX / 2)
+    return KDACONV_EUNSUPPORTED;
+  if ((num_tokens + kChunk - 1) / kChunk + num_seqs > INT32_MAX) return KDACONV_EUNSUPPORTED;
+  if (x_row_stride * 2 * (kChunk + 3) > INT32_MAX) return KDACONV_EUNSUPPORTED;
+  if (num_tokens * part_dim * 2 > INT32_MAX / 2) return KDACONV_EUNSUPPORTED;
+  if (dim * cs1 * 4 > INT32_MAX) return KDACONV_EUNSUPPORTED;
+  if (num_tokens == 0 || num_seqs == 0 || dim == 0) return KDACONV_OK;
+  if (!x || !weight || !conv_states || !qsl || !ci || !out) return KDACONV_EINVAL;
+  if (!aligned16(x) || !aligned16(out)) return KDACONV_EUNSUPPORTED;
+  return KDACONV_OK;
+}
+
+template <int V>
+void launch(const ConvParams& P, int64_t cols, bool bias, bool silu, hipStream_t st) {
+  const dim3 grid((unsigned)((P.num_tokens + kChunk - 1) / kChunk + P.num_seqs),
+                  (unsigned)((cols / V + kWave - 1) / kWave));
+  const dim3 block(kWave);
+  if (bias) {
+    if (silu)
+      hipLaunchKernelGGL((packed_conv_kernel<V, true, true>), grid, block, 0, st, P);
+    else
+      hipLaunchKernelGGL((packed_conv_kernel<V, true, false>), grid, block, 0, st, P);
+  } else {
+    if (silu)
+      hipLaunchKernelGGL((packed_conv_kernel<V, false, true>), grid, block, 0, st, P);
+    else
+      hipLaunchKernelGGL((packed_conv_kernel<V, false, false>), grid, block, 0, st, P);
+  }
+}
+
+}  // namespace
+}  // namespace kdaconv
+
+using namespace kdaconv;
+
+extern "C" int kdaconv_validate(const void* x, int64_t num_tokens, int64_t dim,
+                                int64_t x_row_stride, const float* weight, int64_t weight_stride0,
+                                int64_t weight_stride1, const float* bias,
+                                const float* conv_states, int64_t num_cache_lines,
+                                int64_t cs_stride0, int64_t cs_stride1, int64_t cs_stride2,
+                                const int32_t* query_start_loc, int64_t num_seqs,
+                                const int32_t* cache_indices, int64_t cache_indices_stride,
+                                const uint8_t* has_initial_state, int64_t part_dim, int activation,
+                                int has_null_block, int64_t null_block_id, const void* out) {
+  (void)bias;
+  (void)has_initial_state;
+  (void)has_null_block;
+  (void)null_block_id;
+  return validate(x, num_tokens, dim, x_row_stride, weight, weight_stride0, weight_stride1,
+                  conv_states, num_cache_lines, cs_stride0, cs_stride1, cs_stride2,
+                  query_start_loc, num_seqs, cache_indices, cache_indices_stride, part_dim,
+                  activation, out);
+}
+
+extern "C" int kdaconv_packed_causal_conv1d(
+    const void* x, int64_t num_tokens, int64_t dim, int64_t x_row_stride, const float* weight,
+    int64_t weight_stride0, int64_t weight_stride1, const float* bias, float* conv_states,
+    int64_t num_cache_lines, int64_t cs_stride0, int64_t cs_stride1, int64_t cs_stride2,
+    const int32_t* query_start_loc, int64_t num_seqs, const int32_t* cache_indices,
+    int64_t cache_indices_stride, const uint8_t* has_initial_state, int64_t part_dim,
+    int activation, int has_null_block, int64_t null_block_id, void* out,
+    kdaconv_stream_t stream) {
+  const int rc = validate(x, num_tokens, dim, x_row_stride, weight, weight_stride0,
+                          weight_stride1, conv_states, num_cache_lines, cs_stride0, cs_stride1,
+                          cs_stride2, query_start_loc, num_seqs, cache_indices,
+                          cache_indices_stride, part_dim, activation, out);
+  if (rc != KDACONV_OK || num_tokens == 0 || num_seqs == 0 || dim == 0) return rc;
+
+  ConvParams P;
+  P.x = static_cast<const uint16_t*>(x);
+  P.weight = weight;
+  P.bias = bias;
+  P.states = conv_states;
+  P.qsl = query_start_loc;
+  P.cache_indices = cache_indices;
+  P.has_init = has_initial_state;
+  P.x_row_stride = x_row_stride;
+  P.w_stride0 = weight_stride0;
+  P.w_stride1 = weight_stride1;
+  P.cs_stride0 = cs_stride0;
+  P.cs_stride1 = cs_stride1;
+  P.cs_stride2 = cs_stride2;
+  P.ci_stride = cache_indices_stride;
+  P.num_cache_lines = num_cache_lines;
+  P.plane_stride = num_tokens * part_dim;
+  P.null_block_id = null_block_id;
+  P.num_tokens = (int32_t)num_tokens;
+  P.num_seqs = (int32_t)num_seqs;
+  P.part_dim = (int32_t)part_dim;
+  int levels = 0;
+  int64_t reach = 1;
+  while (reach < num_seqs) {
+    reach *= kWave;
+    ++levels;
+  }
+  P.search_levels = levels;
+  P.search_top = (int32_t)(levels > 0 ? reach / kWave : 1);
+  P.has_null_block = has_null_block != 0;
+
+  // Launches cover groups of whole planes small enough that a lane's offset
+  // into the group's output (planes * num_tokens * part_dim * 2 bytes) stays
+  // below 2^31. One launch in every realistic case.
+  const int64_t plane_bytes = num_tokens * part_dim * 2;
+  const int64_t planes = dim / part_dim;
+  const int64_t per_launch = plane_bytes > 0 ? std::max<int64_t>(1, INT32_MAX / plane_bytes) : planes;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const bool silu = activation == KDACONV_ACT_SILU;
+  for (int64_t pl = 0; pl < planes; pl += per_launch) {
+    const int64_t pe = std::min(planes, pl + per_launch);
+    P.col_begin = (int32_t)(pl * part_dim);
+    P.col_end = (int32_t)(pe * part_dim);
+    P.out = static_cast<uint16_t*>(out) + pl * P.plane_stride;
+    launch<kLaneChannels>(P, (pe - pl) * part_dim, bias != nullptr, silu, st);
+  }
+  return hipGetLastError() == hipSuccess ? KDACONV_OK : KDACONV_ELAUNCH;
+}
+
+extern "C" int kdaconv_activation_map(uint32_t first, int64_t count, int activation,
+                                      uint16_t* out, kdaconv_stream_t stream) {
+  if (count < 0 || count % 8 != 0 || count > ((int64_t)1 << 32)) return KDACONV_EINVAL;
+  if (activation != KDACONV_ACT_NONE && activation != KDACONV_ACT_SILU) return KDACONV_EINVAL;
+  if (count == 0) return KDACONV_OK;
+  if (!out) return KDACONV_EINVAL;
+  if (!aligned16(out)) return KDACONV_EUNSUPPORTED;
+  const uint64_t threads = (uint64_t)count / 8;
+  const dim3 grid((unsigned)((threads + 255) / 256));
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (activation == KDACONV_ACT_SILU)
+    hipLaunchKernelGGL((activation_map_kernel<true>), grid, dim3(256), 0, st, first,
+                       (uint64_t)count, out);
+  else
+    hipLaunchKernelGGL((activation_map_kernel<false>), grid, dim3(256), 0, st, first,
+                       (uint64_t)count, out);
+  return hipGetLastError() == hipSuccess ? KDACONV_OK : KDACONV_ELAUNCH;
+}
+
+extern "C" const char* kdaconv_status_string(int status) {
+  switch (status) {
+    case KDACONV_OK:
+      return "ok";
+    case KDACONV_EINVAL:
+      return "invalid argument";
+    case KDACONV_EUNSUPPORTED:
+      return "unsupported layout or size";
+    case KDACONV_ELAUNCH:
+      return "kernel launch failed";
+    default:
+      return "unknown status";
+  }
+}
+
+extern "C" int kdaconv_version(void) { return 100; }

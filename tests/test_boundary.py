@@ -1,0 +1,113 @@
+"""The C-ABI boundary on the host: the library loads, exports every declared entry
+point, and rejects bad arguments with the documented status codes (no GPU call:
+kdaconv_validate only looks at sizes, strides and pointer values)."""
+
+import ctypes
+import pathlib
+import re
+
+import pytest
+import torch
+
+import packed_varlen_causal_depthwise_amd as kd
+from packed_varlen_causal_depthwise_amd import _lib
+
+HEADER = pathlib.Path(__file__).resolve().parent.parent / "include" / "kdaconv.h"
+
+
+def _declared():
+    text = re.sub(r"/\*.*?\*/", "", HEADER.read_text(), flags=re.S)
+    return sorted(set(re.findall(r"\b(kdaconv_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    names = _declared()
+    assert set(names) == set(_lib.EXPORTS)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_and_version():
+    lib = _lib.load()
+    for code in (0, 1, 2, 3, 99):
+        assert lib.kdaconv_status_string(code)
+    assert lib.kdaconv_version() >= 100
+
+
+# Fake, 256-byte-aligned addresses: kdaconv_validate compares them with NULL and
+# checks their alignment, nothing more.
+A = 0x10000
+
+
+def _args(**kw):
+    a = dict(x=A, T=64, dim=384, sx=384, w=A, ws0=4, ws1=1, b=A, st=A, lines=4, cs0=1152, cs1=3,
+             cs2=1, qsl=A, S=2, ci=A, cis=1, init=A, pd=128, act=1, hn=0, nid=0, out=A)
+    a.update(kw)
+    return [a["x"], a["T"], a["dim"], a["sx"], a["w"], a["ws0"], a["ws1"], a["b"], a["st"],
+            a["lines"], a["cs0"], a["cs1"], a["cs2"], a["qsl"], a["S"], a["ci"], a["cis"],
+            a["init"], a["pd"], a["act"], a["hn"], a["nid"], a["out"]]
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({}, _lib.OK),
+    (dict(T=-1), _lib.EINVAL),
+    (dict(dim=-8), _lib.EINVAL),
+    (dict(S=-1), _lib.EINVAL),
+    (dict(pd=0), _lib.EINVAL),
+    (dict(pd=100), _lib.EINVAL),  # 384 % 100
+    (dict(sx=376), _lib.EINVAL),  # row stride below dim
+    (dict(act=2), _lib.EINVAL),
+    (dict(x=0), _lib.EINVAL),
+    (dict(w=0), _lib.EINVAL),
+    (dict(st=0), _lib.EINVAL),
+    (dict(qsl=0), _lib.EINVAL),
+    (dict(ci=0), _lib.EINVAL),
+    (dict(out=0), _lib.EINVAL),
+    (dict(b=0), _lib.OK),  # no bias
+    (dict(init=0), _lib.OK),  # no initial states
+    (dict(dim=96, sx=96, pd=12), _lib.EUNSUPPORTED),  # part_dim not a multiple of 8
+    (dict(sx=390), _lib.EUNSUPPORTED),  # row stride not a multiple of 8
+    (dict(x=A + 2), _lib.EUNSUPPORTED),  # x not 16-byte aligned
+    (dict(out=A + 8), _lib.EUNSUPPORTED),
+    (dict(cs1=-3), _lib.EUNSUPPORTED),
+    (dict(T=0, x=0, out=0), _lib.OK),  # nothing to do: no launch, pointers unused
+    (dict(S=0, qsl=0), _lib.OK),
+    (dict(T=1 << 31), _lib.EUNSUPPORTED),
+])
+def test_validate_status_codes(kw, code):
+    lib = _lib.load()
+    assert lib.kdaconv_validate(*_args(**kw)) == code
+
+
+def test_activation_map_argument_errors():
+    lib = _lib.load()
+    assert lib.kdaconv_activation_map(0, 7, 1, A, None) == _lib.EINVAL  # not a multiple of 8
+    assert lib.kdaconv_activation_map(0, 8, 5, A, None) == _lib.EINVAL
+    assert lib.kdaconv_activation_map(0, 8, 1, None, None) == _lib.EINVAL
+    assert lib.kdaconv_activation_map(0, 8, 1, A + 2, None) == _lib.EUNSUPPORTED
+    assert lib.kdaconv_activation_map(0, 0, 1, None, None) == _lib.OK
+
+
+def test_python_checks_reject_host_tensors_and_bad_args():
+    x = torch.zeros(4, 16, dtype=torch.bfloat16)
+    w = torch.zeros(16, 4)
+    st = torch.zeros(1, 16, 3)
+    q = torch.tensor([0, 4], dtype=torch.int32)
+    ci = torch.zeros(1, dtype=torch.int32)
+    init = torch.zeros(1, dtype=torch.bool)
+    with pytest.raises(ValueError):
+        kd.packed_causal_conv1d_fn(x, w, None, st, q, ci, init, 8)
+    assert not kd.packed_causal_conv1d_supported(x, w, st, 8)
+    with pytest.raises(ValueError):
+        kd._activation_code("gelu")
+    assert kd._activation_code("swish") == _lib.ACT_SILU
+    assert kd._activation_code(True) == _lib.ACT_SILU
+    assert kd._activation_code(None) == _lib.ACT_NONE
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    monkeypatch.setattr(_lib, "LIBRARY", tmp_path / "absent.so")
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(_lib.LibraryMissing):
+        _lib.load()
