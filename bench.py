@@ -94,6 +94,9 @@ def main() -> int:
     ap.add_argument("--sets", type=int, default=4, help="buffer sets rotated across steps")
     ap.add_argument("--cpu-runs", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="before warm-up, run a plain device-to-device copy of this many MiB "
+                         "three times (a known-size reference for HBM byte counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -132,6 +135,15 @@ def main() -> int:
         s = sets[i % len(sets)]
         kd.packed_causal_conv1d_fn(s["x"], w, b, s["st"], q, ci, init, wl.part_dim, "silu", None,
                                    out=s["out"])
+
+    if args.copy_mib:
+        src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize(dev)
+        del src, dst
 
     for i in range(args.warmup):
         step(i)

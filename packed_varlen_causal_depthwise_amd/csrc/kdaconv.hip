@@ -22,7 +22,10 @@
 // vector address arithmetic runs. A lane keeps the 3 history rows of its
 // channels in registers and a queue of kDepth rows in flight: consuming row r
 // refills its slot with row r + kDepth. Lanes past the launch's last channel
-// (only in a partial last column block) load a valid channel and store nothing.
+// (only in a partial last column block) redo the last active lane's channels:
+// same rows, same weights, and the same state read by the same instruction of
+// the same wave, so they store the same bytes to the same place and the stores
+// need no branch.
 //
 // State. Only the first chunk of a sequence reads the sequence's conv-state
 // line, and the same program writes the updated line after its reads (page,
@@ -43,10 +46,17 @@ constexpr int kChunk = 64;  // tokens per program
 constexpr int kDepth = 8;  // rows in flight per lane
 constexpr int kMinWaves = 4;  // occupancy target: at most 128 VGPRs
 constexpr int kLaneChannels = 4;  // channels per lane (8-byte vectors)
+// Cache-policy bits of the streaming x loads and output stores (gfx950: 1 = sc0,
+// 2 = nt, 16 = sc1).
+constexpr int kLoadPolicy = 0;
+constexpr int kStorePolicy = 0;
+// s_waitcnt immediate (gfx9 encoding) for vmcnt <= kDepth, other counters untouched.
+constexpr int kWaitVm8 = (kDepth & 0xF) | ((kDepth >> 4) << 14) | (0x7 << 4) | (0xF << 8);
 constexpr uint32_t kDescWord3 = 0x00020000u;  // gfx9 raw buffer: 32-bit data format
 constexpr int32_t kRange = 0x7FFFFFFF;
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 template <int V>
 struct Lane;
@@ -55,11 +65,23 @@ template <>
 struct Lane<4> {
   typedef u32x2 vec;
   static __device__ __forceinline__ vec load(__amdgpu_buffer_rsrc_t r, uint32_t vo, uint32_t so) {
-    return __builtin_amdgcn_raw_buffer_load_b64(r, vo, so, 0);
+    return __builtin_amdgcn_raw_buffer_load_b64(r, vo, so, kLoadPolicy);
   }
   static __device__ __forceinline__ void store(vec v, __amdgpu_buffer_rsrc_t r, uint32_t vo,
                                                uint32_t so) {
-    __builtin_amdgcn_raw_buffer_store_b64(v, r, vo, so, 0);
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, vo, so, kStorePolicy);
+  }
+};
+
+template <>
+struct Lane<8> {
+  typedef u32x4 vec;
+  static __device__ __forceinline__ vec load(__amdgpu_buffer_rsrc_t r, uint32_t vo, uint32_t so) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, vo, so, kLoadPolicy);
+  }
+  static __device__ __forceinline__ void store(vec v, __amdgpu_buffer_rsrc_t r, uint32_t vo,
+                                               uint32_t so) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, vo, so, kStorePolicy);
   }
 };
 
@@ -142,7 +164,7 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(kMinWaves
   const int lane = threadIdx.x;
   const int c0 = P.col_begin + (int)(blockIdx.y * kWave + lane) * V;
   const bool active = c0 < P.col_end;
-  const int cl = active ? c0 : P.col_begin;  // inactive lanes compute on a valid channel
+  const int cl = active ? c0 : P.col_end - V;  // inactive lanes redo the last active lane
 
   // Weights and bias first: their addresses do not depend on the search.
   float w0[V], w1[V], w2[V], w3[V], bs[V];
@@ -182,12 +204,6 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(kMinWaves
   const __amdgpu_buffer_rsrc_t orsrc = make_rsrc(P.out + (int64_t)t0 * P.part_dim);
   const uint32_t ovo = (uint32_t)((plane * P.plane_stride + col) * 2);
 
-  // Queue: rows 0 .. kDepth-1 of the chunk.
-  vec q[kDepth];
-#pragma unroll
-  for (int r = 0; r < kDepth; ++r)
-    if (r < n) q[r] = L::load(xr, xvo, (uint32_t)(r + halo) * xrow_bytes);
-
   // History e[t0-3], e[t0-2], e[t0-1].
   float h0[V], h1[V], h2[V];
   bool live = false;
@@ -216,10 +232,21 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(kMinWaves
     unpack<V>(L::load(xr, xvo, 2 * xrow_bytes), h2);
   }
 
+  // Row offsets; rows past the chunk are clamped to its last row, so every
+  // load is in bounds and the number of loads in flight never depends on n.
+  auto row_off = [&](int r) { return (uint32_t)(min(r, n - 1) + halo) * xrow_bytes; };
+
+  // Queue: rows 0 .. kDepth-1 of the chunk, issued after the history loads.
+  vec q[kDepth];
+#pragma unroll
+  for (int r = 0; r < kDepth; ++r) q[r] = L::load(xr, xvo, row_off(r));
+  // The history loads are older than the kDepth queue loads: once at most
+  // kDepth vector memory operations are outstanding, the history has arrived.
+  __builtin_amdgcn_s_waitcnt(kWaitVm8);
+
   // One output row from the widened input row and the history; shifts the history.
-  auto step = [&](vec v, int row) {
-    float xv[V], acc[V];
-    unpack<V>(v, xv);
+  auto step = [&](const float (&xv)[V], int row) {
+    float acc[V];
 #pragma unroll
     for (int k = 0; k < V; ++k) {
       float a = bs[k];
@@ -230,7 +257,7 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(kMinWaves
       acc[k] = a;
     }
     const vec o = activate<kSilu, V>(acc);
-    if (active) L::store(o, orsrc, ovo, (uint32_t)row * orow_bytes);
+    L::store(o, orsrc, ovo, (uint32_t)row * orow_bytes);
 #pragma unroll
     for (int k = 0; k < V; ++k) {
       h0[k] = h1[k];
@@ -244,9 +271,12 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(kMinWaves
   while (n - done >= 2 * kDepth) {
 #pragma unroll
     for (int r = 0; r < kDepth; ++r) {
-      const vec v = q[r];
-      q[r] = L::load(xr, xvo, (uint32_t)(done + kDepth + r + halo) * xrow_bytes);
-      step(v, done + r);
+      float xv[V];
+      unpack<V>(q[r], xv);
+      q[r] = L::load(xr, xvo, row_off(done + kDepth + r));
+      __builtin_amdgcn_sched_barrier(0);
+      step(xv, done + r);
+      __builtin_amdgcn_sched_barrier(0);
     }
     done += kDepth;
   }
@@ -254,16 +284,20 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(kMinWaves
 #pragma unroll
   for (int r = 0; r < kDepth; ++r) {
     if (done + r < n) {
-      const vec v = q[r];
-      if (done + kDepth + r < n)
-        q[r] = L::load(xr, xvo, (uint32_t)(done + kDepth + r + halo) * xrow_bytes);
-      step(v, done + r);
+      float xv[V];
+      unpack<V>(q[r], xv);
+      q[r] = L::load(xr, xvo, row_off(done + kDepth + r));
+      step(xv, done + r);
     }
   }
   done += kDepth;
 #pragma unroll
   for (int r = 0; r < kDepth; ++r)
-    if (done + r < n) step(q[r], done + r);
+    if (done + r < n) {
+      float xv[V];
+      unpack<V>(q[r], xv);
+      step(xv, done + r);
+    }
 
   // Updated state: the last three values of (history ++ x) for this sequence.
   if (j == 0 && live && active) {

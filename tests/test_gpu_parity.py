@@ -68,6 +68,17 @@ def test_dim_not_a_multiple_of_the_wave_width():
     _compare(wl)
 
 
+@pytest.mark.parametrize("parts,part_dim", [(3, 200), (5, 40), (3, 192)])
+def test_partial_last_column_block_with_states(parts, part_dim):
+    """Several column blocks, the last one partial, every sequence starting from its
+    stored state: lanes past the last channel must not disturb other lanes' outputs."""
+    from helpers import make_workload
+
+    wl = make_workload([1, 2, 3, 4, 70, 2], dim=parts * part_dim, part_dim=part_dim, seed=parts,
+                       init=[True] * 6, lines=8, activation=None, bias=False)
+    _compare(wl)
+
+
 def test_empty_calls_touch_nothing():
     import packed_varlen_causal_depthwise_amd as kd
     from helpers import make_workload
