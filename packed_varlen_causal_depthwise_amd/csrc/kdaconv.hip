@@ -46,6 +46,10 @@ constexpr int kChunk = 64;  // tokens per program
 constexpr int kDepth = 8;  // rows in flight per lane
 constexpr int kMinWaves = 4;  // occupancy target: at most 128 VGPRs
 constexpr int kLaneChannels = 4;  // channels per lane (8-byte vectors)
+constexpr int kRowGroup = 2;  // rows whose arithmetic is scheduled together (divides kDepth)
+// Waves lower their issue priority as they progress through their chunk (1) or
+// keep the hardware's oldest-first order (0).
+constexpr int kBalance = 0;
 // Cache-policy bits of the streaming x loads and output stores (gfx950: 1 = sc0,
 // 2 = nt, 16 = sc1).
 constexpr int kLoadPolicy = 0;
@@ -109,6 +113,9 @@ struct ConvParams {
   int32_t search_levels;  // radix-64 levels: smallest L with 64^L >= num_seqs
   int32_t search_top;  // 64^(search_levels - 1)
   int32_t has_null_block;
+  int32_t weight_vec;  // weight is (dim, 4) contiguous and 16-byte aligned
+  int32_t bias_vec;  // bias is 16-byte aligned
+  int32_t state_vec;  // each state line is (dim, 3) contiguous and 16-byte aligned
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
@@ -159,6 +166,7 @@ __device__ __forceinline__ int find_sequence(const ConvParams& P, int p, int lan
 
 template <int V, bool kBias, bool kSilu>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(kMinWaves))) void packed_conv_kernel(const ConvParams P) {
+  static_assert(V == 4, "the vector weight, bias and state paths assume 4 channels per lane");
   typedef Lane<V> L;
   typedef typename L::vec vec;
   const int lane = threadIdx.x;
@@ -166,21 +174,44 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(kMinWaves
   const bool active = c0 < P.col_end;
   const int cl = active ? c0 : P.col_end - V;  // inactive lanes redo the last active lane
 
-  // Weights and bias first: their addresses do not depend on the search.
-  float w0[V], w1[V], w2[V], w3[V], bs[V];
-#pragma unroll
-  for (int k = 0; k < V; ++k) {
-    const float* wp = P.weight + (int64_t)(cl + k) * P.w_stride0;
-    w0[k] = wp[0];
-    w1[k] = wp[P.w_stride1];
-    w2[k] = wp[2 * P.w_stride1];
-    w3[k] = wp[3 * P.w_stride1];
-    bs[k] = kBias ? P.bias[cl + k] : 0.0f;
-  }
-
+  // The program's sequence first (its scalar loads then overlap the vector loads
+  // below), then weights and bias: 16-byte vectors when the layout allows, so a
+  // wave issues a handful of loads instead of one per value.
   const int p = blockIdx.x;
   const int s = find_sequence(P, p, lane);
   if (s < 0) return;
+  float w0[V], w1[V], w2[V], w3[V], bs[V];
+  if (P.weight_vec) {
+    const float4* wp = reinterpret_cast<const float4*>(P.weight + (int64_t)cl * 4);
+#pragma unroll
+    for (int k = 0; k < V; ++k) {
+      const float4 t = wp[k];
+      w0[k] = t.x;
+      w1[k] = t.y;
+      w2[k] = t.z;
+      w3[k] = t.w;
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < V; ++k) {
+      const float* wp = P.weight + (int64_t)(cl + k) * P.w_stride0;
+      w0[k] = wp[0];
+      w1[k] = wp[P.w_stride1];
+      w2[k] = wp[2 * P.w_stride1];
+      w3[k] = wp[3 * P.w_stride1];
+    }
+  }
+  if (kBias && P.bias_vec) {
+    const float4 t = *reinterpret_cast<const float4*>(P.bias + cl);
+    bs[0] = t.x;
+    bs[1] = t.y;
+    bs[2] = t.z;
+    bs[3] = t.w;
+  } else {
+#pragma unroll
+    for (int k = 0; k < V; ++k) bs[k] = kBias ? P.bias[cl + k] : 0.0f;
+  }
+
   const int T = P.num_tokens;
   const int start = min(max(P.qsl[s], 0), T);
   const int end = min(max(P.qsl[s + 1], start), T);
@@ -215,12 +246,22 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(kMinWaves
     const bool init = live && P.has_init != nullptr && P.has_init[s] != 0;
     if (init) {
       const float* sp = P.states + line * P.cs_stride0;
+      if (P.state_vec) {
+        // The lane's 4 channels x 3 values are 12 consecutive floats.
+        const float4* sv = reinterpret_cast<const float4*>(sp + (int64_t)cl * 3);
+        const float4 a = sv[0], b = sv[1], c = sv[2];
+        h0[0] = a.x; h1[0] = a.y; h2[0] = a.z;
+        h0[1] = a.w; h1[1] = b.x; h2[1] = b.y;
+        h0[2] = b.z; h1[2] = b.w; h2[2] = c.x;
+        h0[3] = c.y; h1[3] = c.z; h2[3] = c.w;
+      } else {
 #pragma unroll
-      for (int k = 0; k < V; ++k) {
-        const float* cp = sp + (int64_t)(cl + k) * P.cs_stride1;
-        h0[k] = cp[0];
-        h1[k] = cp[P.cs_stride2];
-        h2[k] = cp[2 * P.cs_stride2];
+        for (int k = 0; k < V; ++k) {
+          const float* cp = sp + (int64_t)(cl + k) * P.cs_stride1;
+          h0[k] = cp[0];
+          h1[k] = cp[P.cs_stride2];
+          h2[k] = cp[2 * P.cs_stride2];
+        }
       }
     } else {
 #pragma unroll
@@ -244,60 +285,103 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(kMinWaves
   // kDepth vector memory operations are outstanding, the history has arrived.
   __builtin_amdgcn_s_waitcnt(kWaitVm8);
 
-  // One output row from the widened input row and the history; shifts the history.
-  auto step = [&](const float (&xv)[V], int row) {
-    float acc[V];
+  // kRowGroup output rows from their widened input rows and the history;
+  // shifts the history. The rows' tap sums are independent, and one rare-path
+  // branch covers all their activations, so their arithmetic can interleave.
+  auto step = [&](const float (&xv)[kRowGroup][V], int row, int rows) {
+    float acc[kRowGroup][V];
 #pragma unroll
-    for (int k = 0; k < V; ++k) {
-      float a = bs[k];
-      a = __builtin_fmaf(w0[k], h0[k], a);
-      a = __builtin_fmaf(w1[k], h1[k], a);
-      a = __builtin_fmaf(w2[k], h2[k], a);
-      a = __builtin_fmaf(w3[k], xv[k], a);
-      acc[k] = a;
+    for (int r = 0; r < kRowGroup; ++r) {
+#pragma unroll
+      for (int k = 0; k < V; ++k) {
+        float a = bs[k];
+        a = __builtin_fmaf(w0[k], h0[k], a);
+        a = __builtin_fmaf(w1[k], h1[k], a);
+        a = __builtin_fmaf(w2[k], h2[k], a);
+        a = __builtin_fmaf(w3[k], xv[r][k], a);
+        acc[r][k] = a;
+      }
+      if (r < rows) {
+#pragma unroll
+        for (int k = 0; k < V; ++k) {
+          h0[k] = h1[k];
+          h1[k] = h2[k];
+          h2[k] = xv[r][k];
+        }
+      }
     }
-    const vec o = activate<kSilu, V>(acc);
-    L::store(o, orsrc, ovo, (uint32_t)row * orow_bytes);
+    uint32_t words[kRowGroup][V / 2];
+    activate_rows<kSilu, V, kRowGroup>(acc, words);
 #pragma unroll
-    for (int k = 0; k < V; ++k) {
-      h0[k] = h1[k];
-      h1[k] = h2[k];
-      h2[k] = xv[k];
+    for (int r = 0; r < kRowGroup; ++r) {
+      if (r < rows) {
+        vec o;
+#pragma unroll
+        for (int i = 0; i < V / 2; ++i) o[i] = words[r][i];
+        L::store(o, orsrc, ovo, (uint32_t)(row + r) * orow_bytes);
+      }
     }
   };
+
+  // The SIMD issues from the oldest ready wave first, so equal chunks started
+  // together would finish far apart and leave each SIMD with too few waves to
+  // hide memory latency at the end. A wave that is ahead yields: its priority
+  // drops by one level per quarter of its chunk.
+  auto set_priority = [&](int done_rows) {
+    if (!kBalance) return;
+    const int level = (done_rows * 4) / n;
+    if (level <= 0)
+      __builtin_amdgcn_s_setprio(3);
+    else if (level == 1)
+      __builtin_amdgcn_s_setprio(2);
+    else if (level == 2)
+      __builtin_amdgcn_s_setprio(1);
+    else
+      __builtin_amdgcn_s_setprio(0);
+  };
+  set_priority(0);
 
   int done = 0;  // rows consumed; the queue holds rows done .. done + kDepth - 1
   // Steady state: every consumed slot is refilled with a row that exists.
   while (n - done >= 2 * kDepth) {
+    set_priority(done);
 #pragma unroll
-    for (int r = 0; r < kDepth; ++r) {
-      float xv[V];
-      unpack<V>(q[r], xv);
-      q[r] = L::load(xr, xvo, row_off(done + kDepth + r));
+    for (int g = 0; g < kDepth; g += kRowGroup) {
+      float xv[kRowGroup][V];
+#pragma unroll
+      for (int r = 0; r < kRowGroup; ++r) {
+        unpack<V>(q[g + r], xv[r]);
+        q[g + r] = L::load(xr, xvo, row_off(done + kDepth + g + r));
+      }
       __builtin_amdgcn_sched_barrier(0);
-      step(xv, done + r);
+      step(xv, done + g, kRowGroup);
       __builtin_amdgcn_sched_barrier(0);
     }
     done += kDepth;
   }
   // Drain: fewer than 2 * kDepth rows remain.
 #pragma unroll
-  for (int r = 0; r < kDepth; ++r) {
-    if (done + r < n) {
-      float xv[V];
-      unpack<V>(q[r], xv);
-      q[r] = L::load(xr, xvo, row_off(done + kDepth + r));
-      step(xv, done + r);
+  for (int g = 0; g < kDepth; g += kRowGroup) {
+    if (done + g < n) {
+      float xv[kRowGroup][V];
+#pragma unroll
+      for (int r = 0; r < kRowGroup; ++r) {
+        unpack<V>(q[g + r], xv[r]);
+        q[g + r] = L::load(xr, xvo, row_off(done + kDepth + g + r));
+      }
+      step(xv, done + g, min(kRowGroup, n - done - g));
     }
   }
   done += kDepth;
 #pragma unroll
-  for (int r = 0; r < kDepth; ++r)
-    if (done + r < n) {
-      float xv[V];
-      unpack<V>(q[r], xv);
-      step(xv, done + r);
+  for (int g = 0; g < kDepth; g += kRowGroup) {
+    if (done + g < n) {
+      float xv[kRowGroup][V];
+#pragma unroll
+      for (int r = 0; r < kRowGroup; ++r) unpack<V>(q[g + r], xv[r]);
+      step(xv, done + g, min(kRowGroup, n - done - g));
     }
+  }
 
   // Updated state: the last three values of (history ++ x) for this sequence.
   if (j == 0 && live && active) {
@@ -309,12 +393,19 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(kMinWaves
       unpack<V>(L::load(tr, xvo, 2 * xrow_bytes), h2);
     }
     float* sp = P.states + line * P.cs_stride0;
+    if (P.state_vec) {
+      float4* sv = reinterpret_cast<float4*>(sp + (int64_t)cl * 3);
+      sv[0] = make_float4(h0[0], h1[0], h2[0], h0[1]);
+      sv[1] = make_float4(h1[1], h2[1], h0[2], h1[2]);
+      sv[2] = make_float4(h2[2], h0[3], h1[3], h2[3]);
+    } else {
 #pragma unroll
-    for (int k = 0; k < V; ++k) {
-      float* cp = sp + (int64_t)(cl + k) * P.cs_stride1;
-      cp[0] = h0[k];
-      cp[P.cs_stride2] = h1[k];
-      cp[2 * P.cs_stride2] = h2[k];
+      for (int k = 0; k < V; ++k) {
+        float* cp = sp + (int64_t)(cl + k) * P.cs_stride1;
+        cp[0] = h0[k];
+        cp[P.cs_stride2] = h1[k];
+        cp[2 * P.cs_stride2] = h2[k];
+      }
     }
   }
 }
@@ -448,6 +539,9 @@ extern "C" int kdaconv_packed_causal_conv1d(
   P.search_levels = levels;
   P.search_top = (int32_t)(levels > 0 ? reach / kWave : 1);
   P.has_null_block = has_null_block != 0;
+  P.weight_vec = weight_stride0 == 4 && weight_stride1 == 1 && aligned16(weight);
+  P.bias_vec = bias != nullptr && aligned16(bias);
+  P.state_vec = cs_stride1 == 3 && cs_stride2 == 1 && cs_stride0 % 4 == 0 && aligned16(conv_states);
 
   // Launches cover groups of whole planes small enough that a lane's offset
   // into the group's output (planes * num_tokens * part_dim * 2 bytes) stays

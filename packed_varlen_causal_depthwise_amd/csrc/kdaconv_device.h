@@ -62,11 +62,23 @@ __device__ __forceinline__ uint32_t bf16_word_exact(float y) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// The exact path is out of line (a call), so its double-precision temporaries do
+// not count against the register budget of the streaming loop that rarely needs
+// it (0 = inline).
+#ifndef KDACONV_EXACT_OUTLINED
+#define KDACONV_EXACT_OUTLINED 1
+#endif
+#if KDACONV_EXACT_OUTLINED
+#define KDACONV_EXACT_INLINE __noinline__
+#else
+#define KDACONV_EXACT_INLINE __forceinline__
+#endif
+
 // The stored word by the defining steps. exp runs in double precision and is
 // rounded once to binary32; the quotient is formed in double from the two binary32
 // operands and rounded once to binary32, which equals the binary32 quotient (53 >=
 // 2 * 24 + 2 bits, so the double rounding is innocuous).
-__device__ __forceinline__ uint32_t act_word_exact(float a, bool silu) {
+__device__ KDACONV_EXACT_INLINE uint32_t act_word_exact(float a, bool silu) {
   float y = a;
   if (silu) {
     const float e = (float)exp(-(double)a);
@@ -76,48 +88,72 @@ __device__ __forceinline__ uint32_t act_word_exact(float a, bool silu) {
   return bf16_word_exact(y);
 }
 
-// N accumulators -> N stored words, two per 32-bit word (element k in half-word
-// k & 1 of word k / 2).
-template <bool kSilu, int N>
-__device__ __forceinline__ void activate_words(const float (&acc)[N], uint32_t (&w)[N / 2]) {
-  float y[N];
+// Does the fast path's word for accumulator a (fast SiLU value y) need the exact path?
+template <bool kSilu>
+__device__ __forceinline__ bool needs_exact(float a, float y) {
+  if (kSilu) return !(a >= kFastSiluMin) | near_bf16_boundary(y);
+  return a != a;
+}
+
+// R rows of N accumulators -> R rows of N stored words, two per 32-bit word
+// (element k of a row in half-word k & 1 of word k / 2). One branch covers the
+// rare exact path of all R * N elements, so the rows' fast paths can overlap.
+template <bool kSilu, int N, int R>
+__device__ __forceinline__ void activate_rows(const float (&acc)[R][N], uint32_t (&w)[R][N / 2]) {
+  float y[R][N];
   bool redo = false;
 #pragma unroll
-  for (int k = 0; k < N; ++k) {
-    if (kSilu) {
-      y[k] = silu_fast(acc[k]);
-      redo |= !(acc[k] >= kFastSiluMin) | near_bf16_boundary(y[k]);
-    } else {
-      y[k] = acc[k];
-      redo |= acc[k] != acc[k];
+  for (int r = 0; r < R; ++r) {
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+      y[r][k] = kSilu ? silu_fast(acc[r][k]) : acc[r][k];
+      redo |= needs_exact<kSilu>(acc[r][k], y[r][k]);
     }
   }
 #pragma unroll
-  for (int i = 0; i < N / 2; ++i) w[i] = pack_bf16x2(y[2 * i], y[2 * i + 1]);
+  for (int r = 0; r < R; ++r) {
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) w[r][i] = pack_bf16x2(y[r][2 * i], y[r][2 * i + 1]);
+  }
   if (__builtin_expect(redo, 0)) {
     // Rare: collect this lane's elements that need the exact path, then run one
     // copy of it per element (selects instead of register-array indexing).
     uint32_t todo = 0;
 #pragma unroll
-    for (int k = 0; k < N; ++k) {
-      const bool r = kSilu ? (!(acc[k] >= kFastSiluMin) | near_bf16_boundary(y[k]))
-                           : (acc[k] != acc[k]);
-      todo |= (uint32_t)r << k;
+    for (int r = 0; r < R; ++r) {
+#pragma unroll
+      for (int k = 0; k < N; ++k) todo |= (uint32_t)needs_exact<kSilu>(acc[r][k], y[r][k]) << (r * N + k);
     }
     while (todo) {
-      const int k = __builtin_ctz(todo);
+      const int e = __builtin_ctz(todo);
       todo &= todo - 1;
-      float a = acc[0];
+      float a = acc[0][0];
 #pragma unroll
-      for (int j = 1; j < N; ++j) a = (k == j) ? acc[j] : a;
+      for (int r = 0; r < R; ++r) {
+#pragma unroll
+        for (int k = 0; k < N; ++k) a = (e == r * N + k) ? acc[r][k] : a;
+      }
       const uint32_t word = act_word_exact(a, kSilu);
+      const int k = e % N;
       const uint32_t shift = (k & 1) * 16;
       const uint32_t keep = ~(0xFFFFu << shift);
       const uint32_t put = word << shift;
 #pragma unroll
-      for (int i = 0; i < N / 2; ++i) w[i] = ((k >> 1) == i) ? ((w[i] & keep) | put) : w[i];
+      for (int r = 0; r < R; ++r) {
+#pragma unroll
+        for (int i = 0; i < N / 2; ++i)
+          w[r][i] = (e == r * N + 2 * i + (k & 1)) ? ((w[r][i] & keep) | put) : w[r][i];
+      }
     }
   }
+}
+
+// N accumulators -> N stored words (one row of activate_rows).
+template <bool kSilu, int N>
+__device__ __forceinline__ void activate_words(const float (&acc)[N], uint32_t (&w)[N / 2]) {
+  const float (&a1)[1][N] = *reinterpret_cast<const float (*)[1][N]>(&acc);
+  uint32_t (&w1)[1][N / 2] = *reinterpret_cast<uint32_t (*)[1][N / 2]>(&w);
+  activate_rows<kSilu, N, 1>(a1, w1);
 }
 
 }  // namespace kdaconv
