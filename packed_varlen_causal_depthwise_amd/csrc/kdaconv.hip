@@ -4,32 +4,35 @@
 // packed_causal_conv1d_fn docstring and source; packed_causal_conv1d_supported)
 // defines the operation; include/kdaconv.h states it in full.
 //
-// Work decomposition. A program is one wave64 handling one token chunk of one
-// sequence over 64 * kLaneChannels channels: each lane owns 4 consecutive
-// channels (an 8-byte bf16 vector), so every x row and every output row moves as
-// one vector per lane, 512 contiguous bytes per wave. Programs are
-// numbered so that sequence s owns programs v(s) .. v(s+1)-1 with
-// v(s) = s + floor(qsl[s] / kChunk); the wave finds its sequence on the device
-// with a radix-64 search over query_start_loc (one ballot per level), so the
-// grid, cdiv(T, kChunk) + num_seqs programs by the column blocks, depends only
-// on host sizes and the launch can be captured in a graph. Chunk j of sequence
-// s covers rows [start + j*kChunk, start + (j+1)*kChunk) of the sequence;
-// programs past the end of their sequence exit at once.
+// Work decomposition. A program is one wave64 handling a tile of kRows
+// consecutive tokens of one sequence over 64 * kLaneChannels channels: each lane
+// owns kLaneChannels consecutive channels, so every x row and every output row of
+// the tile moves as one vector per lane. Programs are numbered so that sequence s
+// owns programs v(s) .. v(s+1)-1 with v(s) = s + floor(qsl[s] / kRows); the wave
+// finds its sequence on the device with a radix-64 search over query_start_loc
+// (one ballot per level), so the grid, cdiv(T, kRows) + num_seqs programs times
+// the column blocks, depends only on host sizes and the launch can be captured in
+// a graph. Tile j of sequence s covers rows [start + j*kRows, start + (j+1)*kRows)
+// of the sequence; programs past the end of their sequence exit at once. The
+// launch is one-dimensional with the column block varying fastest, so waves
+// dispatched together cover whole rows; waves are short, and the dispatcher keeps
+// every SIMD supplied with new ones until the end (long-lived waves started
+// together finish unevenly, since a SIMD issues from its oldest wave first).
 //
-// Streaming. x, out and the state line are addressed through buffer
-// descriptors whose base is the program's first row: the lane's channel offset
-// is a fixed vector register and each row's offset a scalar, so no per-row
-// vector address arithmetic runs. A lane keeps the 3 history rows of its
-// channels in registers and a queue of kDepth rows in flight: consuming row r
-// refills its slot with row r + kDepth. Lanes past the launch's last channel
-// (only in a partial last column block) redo the last active lane's channels:
-// same rows, same weights, and the same state read by the same instruction of
-// the same wave, so they store the same bytes to the same place and the stores
-// need no branch.
+// Memory. A wave issues the loads of its 3 history rows and of all its tile rows
+// before any arithmetic. Tile rows are streamed (nontemporal), except the last
+// three, which the next tile of the column block reads again as its history and
+// which therefore stay cacheable, like the history loads themselves. Outputs are
+// streamed. x and out are addressed through buffer descriptors based at the
+// tile's first row: the lane's channel offset is a fixed vector register and each
+// row's offset a scalar. Lanes past the launch's last channel (only in a partial
+// last column block) redo the last active lane's channels: same rows, same
+// weights, and the same state read by the same instruction of the same wave, so
+// they store the same bytes to the same place and the stores need no branch.
 //
-// State. Only the first chunk of a sequence reads the sequence's conv-state
-// line, and the same program writes the updated line after its reads (page,
-// module docstring).
+// State. Only the first tile of a sequence reads the sequence's conv-state line,
+// and the same program writes the updated line after its reads (page, module
+// docstring).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -42,20 +45,15 @@ namespace kdaconv {
 namespace {
 
 constexpr int kWave = 64;
-constexpr int kChunk = 64;  // tokens per program
-constexpr int kDepth = 8;  // rows in flight per lane
-constexpr int kMinWaves = 4;  // occupancy target: at most 128 VGPRs
+constexpr int kRows = 16;  // tokens per program
 constexpr int kLaneChannels = 4;  // channels per lane (8-byte vectors)
-constexpr int kRowGroup = 2;  // rows whose arithmetic is scheduled together (divides kDepth)
-// Waves lower their issue priority as they progress through their chunk (1) or
-// keep the hardware's oldest-first order (0).
-constexpr int kBalance = 0;
-// Cache-policy bits of the streaming x loads and output stores (gfx950: 1 = sc0,
-// 2 = nt, 16 = sc1).
-constexpr int kLoadPolicy = 0;
-constexpr int kStorePolicy = 0;
-// s_waitcnt immediate (gfx9 encoding) for vmcnt <= kDepth, other counters untouched.
-constexpr int kWaitVm8 = (kDepth & 0xF) | ((kDepth >> 4) << 14) | (0x7 << 4) | (0xF << 8);
+constexpr int kMinWaves = 4;  // occupancy target (waves per SIMD)
+// Fixup list entries per wave (8 bytes each in LDS): room for one row of every
+// lane beyond the entries that trigger a flush.
+constexpr int kFixCapacity = 640;
+// Cache-policy bits of buffer loads and stores (gfx950: 1 = sc0, 2 = nt, 16 = sc1).
+constexpr int kStream = 2;  // nontemporal
+constexpr int kKeep = 0;  // default caching
 constexpr uint32_t kDescWord3 = 0x00020000u;  // gfx9 raw buffer: 32-bit data format
 constexpr int32_t kRange = 0x7FFFFFFF;
 
@@ -68,24 +66,28 @@ struct Lane;
 template <>
 struct Lane<4> {
   typedef u32x2 vec;
+  template <int kPolicy>
   static __device__ __forceinline__ vec load(__amdgpu_buffer_rsrc_t r, uint32_t vo, uint32_t so) {
-    return __builtin_amdgcn_raw_buffer_load_b64(r, vo, so, kLoadPolicy);
+    return __builtin_amdgcn_raw_buffer_load_b64(r, vo, so, kPolicy);
   }
+  template <int kPolicy>
   static __device__ __forceinline__ void store(vec v, __amdgpu_buffer_rsrc_t r, uint32_t vo,
                                                uint32_t so) {
-    __builtin_amdgcn_raw_buffer_store_b64(v, r, vo, so, kStorePolicy);
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, vo, so, kPolicy);
   }
 };
 
 template <>
 struct Lane<8> {
   typedef u32x4 vec;
+  template <int kPolicy>
   static __device__ __forceinline__ vec load(__amdgpu_buffer_rsrc_t r, uint32_t vo, uint32_t so) {
-    return __builtin_amdgcn_raw_buffer_load_b128(r, vo, so, kLoadPolicy);
+    return __builtin_amdgcn_raw_buffer_load_b128(r, vo, so, kPolicy);
   }
+  template <int kPolicy>
   static __device__ __forceinline__ void store(vec v, __amdgpu_buffer_rsrc_t r, uint32_t vo,
                                                uint32_t so) {
-    __builtin_amdgcn_raw_buffer_store_b128(v, r, vo, so, kStorePolicy);
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, vo, so, kPolicy);
   }
 };
 
@@ -109,6 +111,7 @@ struct ConvParams {
   int32_t num_seqs;
   int32_t col_begin;  // first channel of this launch
   int32_t col_end;  // one past its last channel
+  int32_t col_blocks;  // column blocks of 64 * kLaneChannels channels in this launch
   int32_t part_dim;
   int32_t search_levels;  // radix-64 levels: smallest L with 64^L >= num_seqs
   int32_t search_top;  // 64^(search_levels - 1)
@@ -122,26 +125,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, kRange, kDescWord3);
 }
 
+// The widened values pass through an empty asm statement: the compiler cannot
+// recompute them later from the packed word (rematerialization), which would keep
+// the queue slot's registers alive past the refill load.
 template <int V>
 __device__ __forceinline__ void unpack(typename Lane<V>::vec v, float (&f)[V]) {
 #pragma unroll
   for (int i = 0; i < V / 2; ++i) {
     f[2 * i] = widen_lo(v[i]);
     f[2 * i + 1] = widen_hi(v[i]);
+    asm volatile("" : "+v"(f[2 * i]), "+v"(f[2 * i + 1]));
   }
 }
 
-template <bool kSilu, int V>
-__device__ __forceinline__ typename Lane<V>::vec activate(const float (&acc)[V]) {
-  uint32_t u[V / 2];
-  activate_words<kSilu, V>(acc, u);
-  typename Lane<V>::vec w;
-#pragma unroll
-  for (int i = 0; i < V / 2; ++i) w[i] = u[i];
-  return w;
-}
-
-// Largest s in [0, num_seqs) with s + floor(qsl[s] / kChunk) <= p, or -1.
+// Largest s in [0, num_seqs) with s + floor(qsl[s] / kRows) <= p, or -1.
 // v(s) is strictly increasing for a non-decreasing qsl, so at each level the
 // lanes whose candidate passes form a prefix of the wave.
 __device__ __forceinline__ int find_sequence(const ConvParams& P, int p, int lane) {
@@ -152,7 +149,7 @@ __device__ __forceinline__ int find_sequence(const ConvParams& P, int p, int lan
     bool ok = false;
     if (idx < P.num_seqs) {
       const int q = max(P.qsl[idx], 0);
-      ok = idx + q / kChunk <= p;
+      ok = idx + q / kRows <= p;
     }
     const uint64_t m = __ballot(ok);
     const int cnt = __popcll(m);
@@ -160,36 +157,38 @@ __device__ __forceinline__ int find_sequence(const ConvParams& P, int p, int lan
     base += (cnt - 1) * stride;
     stride /= kWave;
   }
-  if (P.search_levels == 0 && max(P.qsl[0], 0) / kChunk > p) return -1;
+  if (P.search_levels == 0 && max(P.qsl[0], 0) / kRows > p) return -1;
   return base;
 }
 
 template <int V, bool kBias, bool kSilu>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(kMinWaves))) void packed_conv_kernel(const ConvParams P) {
-  static_assert(V == 4, "the vector weight, bias and state paths assume 4 channels per lane");
+  static_assert(V % 4 == 0, "the vector weight, bias and state paths take 4 channels at a time");
   typedef Lane<V> L;
   typedef typename L::vec vec;
   const int lane = threadIdx.x;
-  const int c0 = P.col_begin + (int)(blockIdx.y * kWave + lane) * V;
+  const int p = (int)(blockIdx.x / (uint32_t)P.col_blocks);
+  const int cb = (int)(blockIdx.x - (uint32_t)p * (uint32_t)P.col_blocks);
+  const int c0 = P.col_begin + (cb * kWave + lane) * V;
   const bool active = c0 < P.col_end;
   const int cl = active ? c0 : P.col_end - V;  // inactive lanes redo the last active lane
 
-  // The program's sequence first (its scalar loads then overlap the vector loads
-  // below), then weights and bias: 16-byte vectors when the layout allows, so a
-  // wave issues a handful of loads instead of one per value.
-  const int p = blockIdx.x;
   const int s = find_sequence(P, p, lane);
   if (s < 0) return;
+
+  // Weights and bias first: vector memory operations complete in issue order, so
+  // loads issued after the x rows could only be used once all the rows had
+  // arrived. 16-byte vectors when the layout allows.
   float w0[V], w1[V], w2[V], w3[V], bs[V];
   if (P.weight_vec) {
-    const float4* wp = reinterpret_cast<const float4*>(P.weight + (int64_t)cl * 4);
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(P.weight);
 #pragma unroll
     for (int k = 0; k < V; ++k) {
-      const float4 t = wp[k];
-      w0[k] = t.x;
-      w1[k] = t.y;
-      w2[k] = t.z;
-      w3[k] = t.w;
+      const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(wr, (uint32_t)(cl + k) * 16u, 0, kKeep);
+      w0[k] = __uint_as_float(t[0]);
+      w1[k] = __uint_as_float(t[1]);
+      w2[k] = __uint_as_float(t[2]);
+      w3[k] = __uint_as_float(t[3]);
     }
   } else {
 #pragma unroll
@@ -202,11 +201,15 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(kMinWaves
     }
   }
   if (kBias && P.bias_vec) {
-    const float4 t = *reinterpret_cast<const float4*>(P.bias + cl);
-    bs[0] = t.x;
-    bs[1] = t.y;
-    bs[2] = t.z;
-    bs[3] = t.w;
+    const __amdgpu_buffer_rsrc_t br = make_rsrc(P.bias);
+#pragma unroll
+    for (int k = 0; k < V; k += 4) {
+      const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(br, (uint32_t)(cl + k) * 4u, 0, kKeep);
+      bs[k] = __uint_as_float(t[0]);
+      bs[k + 1] = __uint_as_float(t[1]);
+      bs[k + 2] = __uint_as_float(t[2]);
+      bs[k + 3] = __uint_as_float(t[3]);
+    }
   } else {
 #pragma unroll
     for (int k = 0; k < V; ++k) bs[k] = kBias ? P.bias[cl + k] : 0.0f;
@@ -216,26 +219,14 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(kMinWaves
   const int start = min(max(P.qsl[s], 0), T);
   const int end = min(max(P.qsl[s + 1], start), T);
   const int len = end - start;
-  const int j = p - (s + start / kChunk);
-  if ((int64_t)j * kChunk >= len) return;  // past the end of its sequence
-  const int t0 = start + j * kChunk;
-  const int n = min(kChunk, end - t0);
+  const int j = p - (s + start / kRows);
+  if ((int64_t)j * kRows >= len) return;  // past the end of its sequence
+  const int t0 = start + j * kRows;
+  const int n = min(kRows, end - t0);
 
-  // x descriptor based at row t0 - 3 (later chunks read 3 history rows) or t0.
-  const int halo = j > 0 ? 3 : 0;
-  const uint32_t xrow_bytes = (uint32_t)(P.x_row_stride * 2);
-  const __amdgpu_buffer_rsrc_t xr = make_rsrc(P.x + (int64_t)(t0 - halo) * P.x_row_stride);
-  const uint32_t xvo = (uint32_t)(cl * 2);
-
-  // out descriptor based at row t0 of the launch's first plane; the lane's
-  // plane and column go into its fixed offset.
-  const int plane = (cl - P.col_begin) / P.part_dim;
-  const int col = (cl - P.col_begin) - plane * P.part_dim;
-  const uint32_t orow_bytes = (uint32_t)(P.part_dim * 2);
-  const __amdgpu_buffer_rsrc_t orsrc = make_rsrc(P.out + (int64_t)t0 * P.part_dim);
-  const uint32_t ovo = (uint32_t)((plane * P.plane_stride + col) * 2);
-
-  // History e[t0-3], e[t0-2], e[t0-1].
+  // History e[t0-3], e[t0-2], e[t0-1]: the stored state for the first tile of a
+  // live sequence with an initial state, zeros for other first tiles (loaded here,
+  // before the x rows), x rows otherwise (below).
   float h0[V], h1[V], h2[V];
   bool live = false;
   int64_t line = 0;
@@ -247,13 +238,23 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(kMinWaves
     if (init) {
       const float* sp = P.states + line * P.cs_stride0;
       if (P.state_vec) {
-        // The lane's 4 channels x 3 values are 12 consecutive floats.
-        const float4* sv = reinterpret_cast<const float4*>(sp + (int64_t)cl * 3);
-        const float4 a = sv[0], b = sv[1], c = sv[2];
-        h0[0] = a.x; h1[0] = a.y; h2[0] = a.z;
-        h0[1] = a.w; h1[1] = b.x; h2[1] = b.y;
-        h0[2] = b.z; h1[2] = b.w; h2[2] = c.x;
-        h0[3] = c.y; h1[3] = c.z; h2[3] = c.w;
+        // The lane's V channels x 3 values are 3V consecutive floats.
+        const __amdgpu_buffer_rsrc_t sr = make_rsrc(sp);
+        float f[3 * V];
+#pragma unroll
+        for (int i = 0; i < 3 * V / 4; ++i) {
+          const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(sr, (uint32_t)cl * 12u + 16u * i, 0, kKeep);
+          f[4 * i] = __uint_as_float(t[0]);
+          f[4 * i + 1] = __uint_as_float(t[1]);
+          f[4 * i + 2] = __uint_as_float(t[2]);
+          f[4 * i + 3] = __uint_as_float(t[3]);
+        }
+#pragma unroll
+        for (int k = 0; k < V; ++k) {
+          h0[k] = f[3 * k];
+          h1[k] = f[3 * k + 1];
+          h2[k] = f[3 * k + 2];
+        }
       } else {
 #pragma unroll
         for (int k = 0; k < V; ++k) {
@@ -267,137 +268,117 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(kMinWaves
 #pragma unroll
       for (int k = 0; k < V; ++k) h0[k] = h1[k] = h2[k] = 0.0f;
     }
+  }
+
+
+  // x descriptor based at row t0 - 3 (later tiles read 3 history rows) or t0.
+  const int halo = j > 0 ? 3 : 0;
+  const uint32_t xrow_bytes = (uint32_t)(P.x_row_stride * 2);
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(P.x + (int64_t)(t0 - halo) * P.x_row_stride);
+  const uint32_t xvo = (uint32_t)(cl * 2);
+
+  // All loads of x first: the history rows, then the tile rows (rows past the
+  // tile's end repeat its last row, so every load is in bounds).
+  vec hraw[3];
+  if (halo) {
+#pragma unroll
+    for (int r = 0; r < 3; ++r) hraw[r] = L::template load<kKeep>(xr, xvo, (uint32_t)r * xrow_bytes);
+  }
+  vec q[kRows];
+#pragma unroll
+  for (int r = 0; r < kRows; ++r) {
+    const uint32_t off = (uint32_t)(min(r, n - 1) + halo) * xrow_bytes;
+    q[r] = r < kRows - 3 ? L::template load<kStream>(xr, xvo, off) : L::template load<kKeep>(xr, xvo, off);
+  }
+
+  if (halo) {
+    unpack<V>(hraw[0], h0);
+    unpack<V>(hraw[1], h1);
+    unpack<V>(hraw[2], h2);
+  }
+
+  // out descriptor based at row t0 of the launch's first plane; the lane's
+  // plane and column go into its fixed offset.
+  const int plane = (cl - P.col_begin) / P.part_dim;
+  const int col = (cl - P.col_begin) - plane * P.part_dim;
+  const uint32_t orow_bytes = (uint32_t)(P.part_dim * 2);
+  const __amdgpu_buffer_rsrc_t orsrc = make_rsrc(P.out + (int64_t)t0 * P.part_dim);
+  const uint32_t ovo = (uint32_t)((plane * P.plane_stride + col) * 2);
+
+  // Elements needing the exact path, rewritten in batches (FixupList).
+  __shared__ uint2 fix_slots[kFixCapacity];
+  FixupList<kFixCapacity> fix{fix_slots, 0u};
+  auto fix_store = [&](uint32_t word, uint32_t offset) {
+    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)word, orsrc, offset, 0, kStream);
+  };
+
+  // Row r of the tile: taps, activation, store, history shift.
+  auto row = [&](int r) {
+    float xv[V];
+    unpack<V>(q[r], xv);
+    float acc[1][V];
+#pragma unroll
+    for (int k = 0; k < V; ++k) {
+      float a = bs[k];
+      a = __builtin_fmaf(w0[k], h0[k], a);
+      a = __builtin_fmaf(w1[k], h1[k], a);
+      a = __builtin_fmaf(w2[k], h2[k], a);
+      a = __builtin_fmaf(w3[k], xv[k], a);
+      acc[0][k] = a;
+      h0[k] = h1[k];
+      h1[k] = h2[k];
+      h2[k] = xv[k];
+    }
+    uint32_t words[1][V / 2];
+    float y[1][V];
+    const bool check = activate_rows<kSilu, V, 1>(acc, y, words);
+    vec o;
+#pragma unroll
+    for (int i = 0; i < V / 2; ++i) o[i] = words[0][i];
+    L::template store<kStream>(o, orsrc, ovo, (uint32_t)r * orow_bytes);
+    // Rare (any lane): record the elements whose fast word may be wrong; they are
+    // rewritten when the list is flushed.
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(check) != 0, 0)) {
+      if (!fix.fits(V * kWave)) fix.template flush<kSilu>(lane, fix_store);
+#pragma unroll
+      for (int k = 0; k < V; ++k)
+        fix.append(needs_exact<kSilu>(acc[0][k], y[0][k]), acc[0][k],
+                   ovo + 2u * k + (uint32_t)r * orow_bytes);
+    }
+  };
+  if (n == kRows) {
+    // Full tile: straight-line code, no conditions.
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) row(r);
   } else {
-    unpack<V>(L::load(xr, xvo, 0), h0);
-    unpack<V>(L::load(xr, xvo, xrow_bytes), h1);
-    unpack<V>(L::load(xr, xvo, 2 * xrow_bytes), h2);
+#pragma unroll
+    for (int r = 0; r < kRows; ++r)
+      if (r < n) row(r);
   }
-
-  // Row offsets; rows past the chunk are clamped to its last row, so every
-  // load is in bounds and the number of loads in flight never depends on n.
-  auto row_off = [&](int r) { return (uint32_t)(min(r, n - 1) + halo) * xrow_bytes; };
-
-  // Queue: rows 0 .. kDepth-1 of the chunk, issued after the history loads.
-  vec q[kDepth];
-#pragma unroll
-  for (int r = 0; r < kDepth; ++r) q[r] = L::load(xr, xvo, row_off(r));
-  // The history loads are older than the kDepth queue loads: once at most
-  // kDepth vector memory operations are outstanding, the history has arrived.
-  __builtin_amdgcn_s_waitcnt(kWaitVm8);
-
-  // kRowGroup output rows from their widened input rows and the history;
-  // shifts the history. The rows' tap sums are independent, and one rare-path
-  // branch covers all their activations, so their arithmetic can interleave.
-  auto step = [&](const float (&xv)[kRowGroup][V], int row, int rows) {
-    float acc[kRowGroup][V];
-#pragma unroll
-    for (int r = 0; r < kRowGroup; ++r) {
-#pragma unroll
-      for (int k = 0; k < V; ++k) {
-        float a = bs[k];
-        a = __builtin_fmaf(w0[k], h0[k], a);
-        a = __builtin_fmaf(w1[k], h1[k], a);
-        a = __builtin_fmaf(w2[k], h2[k], a);
-        a = __builtin_fmaf(w3[k], xv[r][k], a);
-        acc[r][k] = a;
-      }
-      if (r < rows) {
-#pragma unroll
-        for (int k = 0; k < V; ++k) {
-          h0[k] = h1[k];
-          h1[k] = h2[k];
-          h2[k] = xv[r][k];
-        }
-      }
-    }
-    uint32_t words[kRowGroup][V / 2];
-    activate_rows<kSilu, V, kRowGroup>(acc, words);
-#pragma unroll
-    for (int r = 0; r < kRowGroup; ++r) {
-      if (r < rows) {
-        vec o;
-#pragma unroll
-        for (int i = 0; i < V / 2; ++i) o[i] = words[r][i];
-        L::store(o, orsrc, ovo, (uint32_t)(row + r) * orow_bytes);
-      }
-    }
-  };
-
-  // The SIMD issues from the oldest ready wave first, so equal chunks started
-  // together would finish far apart and leave each SIMD with too few waves to
-  // hide memory latency at the end. A wave that is ahead yields: its priority
-  // drops by one level per quarter of its chunk.
-  auto set_priority = [&](int done_rows) {
-    if (!kBalance) return;
-    const int level = (done_rows * 4) / n;
-    if (level <= 0)
-      __builtin_amdgcn_s_setprio(3);
-    else if (level == 1)
-      __builtin_amdgcn_s_setprio(2);
-    else if (level == 2)
-      __builtin_amdgcn_s_setprio(1);
-    else
-      __builtin_amdgcn_s_setprio(0);
-  };
-  set_priority(0);
-
-  int done = 0;  // rows consumed; the queue holds rows done .. done + kDepth - 1
-  // Steady state: every consumed slot is refilled with a row that exists.
-  while (n - done >= 2 * kDepth) {
-    set_priority(done);
-#pragma unroll
-    for (int g = 0; g < kDepth; g += kRowGroup) {
-      float xv[kRowGroup][V];
-#pragma unroll
-      for (int r = 0; r < kRowGroup; ++r) {
-        unpack<V>(q[g + r], xv[r]);
-        q[g + r] = L::load(xr, xvo, row_off(done + kDepth + g + r));
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      step(xv, done + g, kRowGroup);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    done += kDepth;
-  }
-  // Drain: fewer than 2 * kDepth rows remain.
-#pragma unroll
-  for (int g = 0; g < kDepth; g += kRowGroup) {
-    if (done + g < n) {
-      float xv[kRowGroup][V];
-#pragma unroll
-      for (int r = 0; r < kRowGroup; ++r) {
-        unpack<V>(q[g + r], xv[r]);
-        q[g + r] = L::load(xr, xvo, row_off(done + kDepth + g + r));
-      }
-      step(xv, done + g, min(kRowGroup, n - done - g));
-    }
-  }
-  done += kDepth;
-#pragma unroll
-  for (int g = 0; g < kDepth; g += kRowGroup) {
-    if (done + g < n) {
-      float xv[kRowGroup][V];
-#pragma unroll
-      for (int r = 0; r < kRowGroup; ++r) unpack<V>(q[g + r], xv[r]);
-      step(xv, done + g, min(kRowGroup, n - done - g));
-    }
-  }
+  fix.template flush<kSilu>(lane, fix_store);
 
   // Updated state: the last three values of (history ++ x) for this sequence.
   if (j == 0 && live && active) {
     if (t0 + n < end) {
-      // The sequence continues past this chunk: its last rows are end-3 .. end-1.
+      // The sequence continues past this tile: its last rows are end-3 .. end-1.
       const __amdgpu_buffer_rsrc_t tr = make_rsrc(P.x + (int64_t)(end - 3) * P.x_row_stride);
-      unpack<V>(L::load(tr, xvo, 0), h0);
-      unpack<V>(L::load(tr, xvo, xrow_bytes), h1);
-      unpack<V>(L::load(tr, xvo, 2 * xrow_bytes), h2);
+      unpack<V>(L::template load<kKeep>(tr, xvo, 0), h0);
+      unpack<V>(L::template load<kKeep>(tr, xvo, xrow_bytes), h1);
+      unpack<V>(L::template load<kKeep>(tr, xvo, 2 * xrow_bytes), h2);
     }
     float* sp = P.states + line * P.cs_stride0;
     if (P.state_vec) {
+      float f[3 * V];
+#pragma unroll
+      for (int k = 0; k < V; ++k) {
+        f[3 * k] = h0[k];
+        f[3 * k + 1] = h1[k];
+        f[3 * k + 2] = h2[k];
+      }
       float4* sv = reinterpret_cast<float4*>(sp + (int64_t)cl * 3);
-      sv[0] = make_float4(h0[0], h1[0], h2[0], h0[1]);
-      sv[1] = make_float4(h1[1], h2[1], h0[2], h1[2]);
-      sv[2] = make_float4(h2[2], h0[3], h1[3], h2[3]);
+#pragma unroll
+      for (int i = 0; i < 3 * V / 4; ++i)
+        sv[i] = make_float4(f[4 * i], f[4 * i + 1], f[4 * i + 2], f[4 * i + 3]);
     } else {
 #pragma unroll
       for (int k = 0; k < V; ++k) {
@@ -410,19 +391,38 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(kMinWaves
   }
 }
 
-// The activation map on consecutive FP32 bit patterns, 8 per thread, through
-// the same activate_words the convolution uses.
+// The activation map on consecutive FP32 bit patterns, 8 per lane as two rows of 4,
+// through the same activate_rows, needs_exact and FixupList code the convolution
+// uses (one wave per block, so each block owns its list).
 template <bool kSilu>
-__global__ __launch_bounds__(256) void activation_map_kernel(uint32_t first, uint64_t count,
-                                                             uint16_t* __restrict__ out) {
-  const uint64_t i = ((uint64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+__global__ __launch_bounds__(kWave) void activation_map_kernel(uint32_t first, uint64_t count,
+                                                               uint16_t* __restrict__ out) {
+  const int lane = threadIdx.x;
+  const uint64_t block_first = (uint64_t)blockIdx.x * kWave * 8;
+  const uint64_t i = block_first + (uint64_t)lane * 8;
   if (i >= count) return;
-  float acc[8];
+  float acc[2][4], y[2][4];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) acc[k] = __uint_as_float(first + (uint32_t)(i + k));
-  uint32_t w[4];
-  activate_words<kSilu, 8>(acc, w);
-  *reinterpret_cast<uint4*>(out + i) = make_uint4(w[0], w[1], w[2], w[3]);
+  for (int r = 0; r < 2; ++r) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) acc[r][k] = __uint_as_float(first + (uint32_t)(i + 4 * r + k));
+  }
+  uint32_t w[2][2];
+  const bool check = activate_rows<kSilu, 4, 2>(acc, y, w);
+  *reinterpret_cast<uint4*>(out + i) = make_uint4(w[0][0], w[0][1], w[1][0], w[1][1]);
+  __shared__ uint2 fix_slots[kFixCapacity];
+  FixupList<kFixCapacity> fix{fix_slots, 0u};
+  uint16_t* const block_out = out + block_first;
+  auto fix_store = [&](uint32_t word, uint32_t offset) { block_out[offset] = (uint16_t)word; };
+  if (__builtin_amdgcn_ballot_w64(check) != 0) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        fix.append(needs_exact<kSilu>(acc[r][k], y[r][k]), acc[r][k], (uint32_t)lane * 8 + 4 * r + k);
+    }
+  }
+  fix.template flush<kSilu>(lane, fix_store);
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -443,8 +443,9 @@ int validate(const void* x, int64_t num_tokens, int64_t dim, int64_t x_row_strid
   // and within one output plane.
   if (num_tokens > INT32_MAX - 1 || num_seqs > INT32_MAX / 2 || dim > INT32_MAX / 2)
     return KDACONV_EUNSUPPORTED;
-  if ((num_tokens + kChunk - 1) / kChunk + num_seqs > INT32_MAX) return KDACONV_EUNSUPPORTED;
-  if (x_row_stride * 2 * (kChunk + 3) > INT32_MAX) return KDACONV_EUNSUPPORTED;
+  if (((num_tokens + kRows - 1) / kRows + num_seqs) * ((dim + kWave * kLaneChannels - 1) / (kWave * kLaneChannels)) > INT32_MAX)
+    return KDACONV_EUNSUPPORTED;
+  if (x_row_stride * 2 * (kRows + 3) > INT32_MAX) return KDACONV_EUNSUPPORTED;
   if (num_tokens * part_dim * 2 > INT32_MAX / 2) return KDACONV_EUNSUPPORTED;
   if (dim * cs1 * 4 > INT32_MAX) return KDACONV_EUNSUPPORTED;
   if (num_tokens == 0 || num_seqs == 0 || dim == 0) return KDACONV_OK;
@@ -454,9 +455,10 @@ int validate(const void* x, int64_t num_tokens, int64_t dim, int64_t x_row_strid
 }
 
 template <int V>
-void launch(const ConvParams& P, int64_t cols, bool bias, bool silu, hipStream_t st) {
-  const dim3 grid((unsigned)((P.num_tokens + kChunk - 1) / kChunk + P.num_seqs),
-                  (unsigned)((cols / V + kWave - 1) / kWave));
+void launch(ConvParams P, int64_t cols, bool bias, bool silu, hipStream_t st) {
+  P.col_blocks = (int32_t)((cols / V + kWave - 1) / kWave);
+  const uint64_t programs = (uint64_t)(P.num_tokens + kRows - 1) / kRows + (uint64_t)P.num_seqs;
+  const dim3 grid((unsigned)(programs * (uint64_t)P.col_blocks));
   const dim3 block(kWave);
   if (bias) {
     if (silu)
@@ -569,13 +571,13 @@ extern "C" int kdaconv_activation_map(uint32_t first, int64_t count, int activat
   if (!out) return KDACONV_EINVAL;
   if (!aligned16(out)) return KDACONV_EUNSUPPORTED;
   const uint64_t threads = (uint64_t)count / 8;
-  const dim3 grid((unsigned)((threads + 255) / 256));
+  const dim3 grid((unsigned)((threads + kWave - 1) / kWave));
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (activation == KDACONV_ACT_SILU)
-    hipLaunchKernelGGL((activation_map_kernel<true>), grid, dim3(256), 0, st, first,
+    hipLaunchKernelGGL((activation_map_kernel<true>), grid, dim3(kWave), 0, st, first,
                        (uint64_t)count, out);
   else
-    hipLaunchKernelGGL((activation_map_kernel<false>), grid, dim3(256), 0, st, first,
+    hipLaunchKernelGGL((activation_map_kernel<false>), grid, dim3(kWave), 0, st, first,
                        (uint64_t)count, out);
   return hipGetLastError() == hipSuccess ? KDACONV_OK : KDACONV_ELAUNCH;
 }

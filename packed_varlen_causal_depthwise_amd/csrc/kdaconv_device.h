@@ -10,10 +10,10 @@
 // hardware exp2 and reciprocal (a few FP32 ulps off the binary32 SiLU) and the
 // word it rounds to is kept whenever the fast value is farther than that error
 // bound from a bf16 rounding boundary: then the binary32 SiLU lies on the same
-// side and rounds to the same word. The rare rest (and NaN, and a < kFastSiluMin
-// where the fast exp argument loses accuracy) goes through an exact evaluation in
-// double precision. The map from every FP32 input to its word is checked against
-// the CPU reference on all 2^32 inputs.
+// side and rounds to the same word. The rare rest (and NaN, and large negative
+// accumulators, where the rounded exp2 argument loses accuracy) goes through an
+// exact evaluation in double precision. The map from every FP32 input to its word
+// is checked against the CPU reference on all 2^32 inputs.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -24,12 +24,16 @@ namespace kdaconv {
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-// Smallest accumulator the fast SiLU serves; below it, and for NaN, the exact path runs.
-constexpr float kFastSiluMin = -8.0f;
 // Bound, in FP32 ulps (distance between bit patterns), on |fast SiLU - binary32 SiLU|
-// for kFastSiluMin <= a. Fast values within this many ulps of a bf16 rounding
-// boundary are recomputed exactly.
+// wherever the fast path is trusted. Fast values within this many ulps of a bf16
+// rounding boundary are recomputed exactly.
 constexpr uint32_t kSiluUlpBound = 16;
+// The fast path is trusted while its exp2 result stays below 2048, which holds for
+// every a above about -7.6 (the product a * -log2(e) is rounded before the exp2, an
+// error that grows with |a|). Larger results, and NaN (either sign), are taken by
+// the exact path. Compared as bit patterns: exp2 never returns a negative number,
+// and every NaN pattern lies above the threshold.
+constexpr uint32_t kFastExpLimitBits = 0x45000000u;  // 2048.0f
 
 // bf16 -> FP32 is exact: the bf16 pattern is the upper half of the FP32 word.
 __device__ __forceinline__ float widen_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -41,18 +45,27 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
-// SiLU from the hardware exp2 and reciprocal; a few ulps from the binary32 value
-// for a >= kFastSiluMin.
-__device__ __forceinline__ float silu_fast(float a) {
-  const float e = __builtin_amdgcn_exp2f(a * -1.44269504088896341f);
+// SiLU from the hardware exp2 and reciprocal; e receives the exp2 result, which
+// decides whether the value can be trusted (kFastExpLimitBits).
+__device__ __forceinline__ float silu_fast(float a, float& e) {
+  e = __builtin_amdgcn_exp2f(a * -1.44269504088896341f);
   return a * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
-// True when y lies within kSiluUlpBound ulps of a point halfway between two bf16
-// numbers (its low half-word within the bound of 0x8000).
-__device__ __forceinline__ bool near_bf16_boundary(float y) {
-  const uint32_t u = __float_as_uint(y);
-  return ((u + (0x8000u + kSiluUlpBound)) << 16) <= ((2u * kSiluUlpBound) << 16);
+// Key of a fast value: its low half-word moved to the top plus an offset, so that
+// the key is at least kNearKey exactly when the half-word lies within
+// kSiluUlpBound of 0x8000, the point halfway between two bf16 numbers.
+constexpr uint32_t kNearKey = (0x10000u - 2u * kSiluUlpBound - 1u) << 16;
+constexpr uint32_t kNearOffset = 0u - ((0x8000u + kSiluUlpBound + 1u) << 16);
+__device__ __forceinline__ uint32_t near_key(float y) {
+  return (__float_as_uint(y) << 16) + kNearOffset;
+}
+// The same key in one instruction (the compiler emits a shift and an add, since the
+// fused form takes no literal operand): offset must hold kNearOffset.
+__device__ __forceinline__ uint32_t near_key_fused(float y, uint32_t offset) {
+  uint32_t key;
+  asm("v_lshl_add_u32 %0, %1, 16, %2" : "=v"(key) : "v"(y), "s"(offset));
+  return key;
 }
 
 // FP32 -> bf16 word, round to nearest even, NaN -> 0x7FC0.
@@ -88,26 +101,45 @@ __device__ KDACONV_EXACT_INLINE uint32_t act_word_exact(float a, bool silu) {
   return bf16_word_exact(y);
 }
 
-// Does the fast path's word for accumulator a (fast SiLU value y) need the exact path?
+// Accumulators at or below this bound take the exact path. Every a with exp2 result
+// at least 2048 (kFastExpLimitBits) lies below about -7.62, so the per-element test
+// below flags a superset of what the reduction in activate_rows detects.
+constexpr float kExactBelow = -7.5f;
+
+// Does the fast word of accumulator a (fast value y) need the exact path? SiLU:
+// y near a bf16 rounding boundary, or a below kExactBelow, or NaN; identity: NaN.
 template <bool kSilu>
 __device__ __forceinline__ bool needs_exact(float a, float y) {
-  if (kSilu) return !(a >= kFastSiluMin) | near_bf16_boundary(y);
+  if (kSilu) return near_key(y) >= kNearKey || !(a >= kExactBelow);
   return a != a;
 }
 
-// R rows of N accumulators -> R rows of N stored words, two per 32-bit word
-// (element k of a row in half-word k & 1 of word k / 2). One branch covers the
-// rare exact path of all R * N elements, so the rows' fast paths can overlap.
+// R rows of N accumulators -> R rows of N fast words, two per 32-bit word (element k
+// of a row in half-word k & 1 of word k / 2); y receives the fast values. Returns
+// whether any element may need the exact path. The test is a reduction over all
+// R * N elements (unsigned maxima of the keys and of the exp2 bit patterns; for the
+// identity, a sum that is NaN if any term is) followed by one compare, so it costs
+// about one instruction per element; a true result is followed by needs_exact on
+// each element.
 template <bool kSilu, int N, int R>
-__device__ __forceinline__ void activate_rows(const float (&acc)[R][N], uint32_t (&w)[R][N / 2]) {
-  float y[R][N];
-  bool redo = false;
+__device__ __forceinline__ bool activate_rows(const float (&acc)[R][N], float (&y)[R][N],
+                                              uint32_t (&w)[R][N / 2]) {
+  const uint32_t offset = kNearOffset;
+  uint32_t key_max = 0, exp_max = 0;
+  float sum = 0.0f;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
 #pragma unroll
     for (int k = 0; k < N; ++k) {
-      y[r][k] = kSilu ? silu_fast(acc[r][k]) : acc[r][k];
-      redo |= needs_exact<kSilu>(acc[r][k], y[r][k]);
+      if (kSilu) {
+        float e;
+        y[r][k] = silu_fast(acc[r][k], e);
+        key_max = max(key_max, near_key_fused(y[r][k], offset));
+        exp_max = max(exp_max, __float_as_uint(e));
+      } else {
+        y[r][k] = acc[r][k];
+        sum += acc[r][k];
+      }
     }
   }
 #pragma unroll
@@ -115,45 +147,52 @@ __device__ __forceinline__ void activate_rows(const float (&acc)[R][N], uint32_t
 #pragma unroll
     for (int i = 0; i < N / 2; ++i) w[r][i] = pack_bf16x2(y[r][2 * i], y[r][2 * i + 1]);
   }
-  if (__builtin_expect(redo, 0)) {
-    // Rare: collect this lane's elements that need the exact path, then run one
-    // copy of it per element (selects instead of register-array indexing).
-    uint32_t todo = 0;
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-#pragma unroll
-      for (int k = 0; k < N; ++k) todo |= (uint32_t)needs_exact<kSilu>(acc[r][k], y[r][k]) << (r * N + k);
-    }
-    while (todo) {
-      const int e = __builtin_ctz(todo);
-      todo &= todo - 1;
-      float a = acc[0][0];
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-#pragma unroll
-        for (int k = 0; k < N; ++k) a = (e == r * N + k) ? acc[r][k] : a;
-      }
-      const uint32_t word = act_word_exact(a, kSilu);
-      const int k = e % N;
-      const uint32_t shift = (k & 1) * 16;
-      const uint32_t keep = ~(0xFFFFu << shift);
-      const uint32_t put = word << shift;
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-#pragma unroll
-        for (int i = 0; i < N / 2; ++i)
-          w[r][i] = (e == r * N + 2 * i + (k & 1)) ? ((w[r][i] & keep) | put) : w[r][i];
-      }
-    }
-  }
+  return kSilu ? (key_max >= kNearKey || exp_max >= kFastExpLimitBits) : sum != sum;
 }
 
-// N accumulators -> N stored words (one row of activate_rows).
-template <bool kSilu, int N>
-__device__ __forceinline__ void activate_words(const float (&acc)[N], uint32_t (&w)[N / 2]) {
-  const float (&a1)[1][N] = *reinterpret_cast<const float (*)[1][N]>(&acc);
-  uint32_t (&w1)[1][N / 2] = *reinterpret_cast<uint32_t (*)[1][N / 2]>(&w);
-  activate_rows<kSilu, N, 1>(a1, w1);
-}
+// Elements whose fast word must be replaced, collected per wave in LDS and
+// rewritten with their exact words in passes of 64 (one per lane). Deferring
+// them lets a wave run the exact path once for the elements of many rows instead
+// of once per row group in which any of its 64 lanes needs it. A flush first waits
+// for the wave's earlier stores, so each exact word lands after the fast word it
+// replaces. count is uniform across the wave.
+template <int kCapacity>
+struct FixupList {
+  uint2* slots;  // kCapacity entries {accumulator bits, output offset} in LDS
+  uint32_t count;
+
+  // Appends {acc, offset} for every lane where flag holds.
+  __device__ __forceinline__ void append(bool flag, float acc, uint32_t offset) {
+    const uint64_t mask = __ballot(flag);
+    if (mask == 0) return;
+    if (flag) {
+      const uint32_t below = __builtin_amdgcn_mbcnt_hi(
+          (uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+      slots[count + below] = make_uint2(__float_as_uint(acc), offset);
+    }
+    count += (uint32_t)__popcll(mask);
+  }
+
+  // Whether appends of up to `incoming` more entries still fit.
+  __device__ __forceinline__ bool fits(uint32_t incoming) const {
+    return count + incoming <= (uint32_t)kCapacity;
+  }
+
+  // Writes the exact word of every entry through store(word, offset) and empties
+  // the list.
+  template <bool kSilu, class Store>
+  __device__ __forceinline__ void flush(int lane, Store store) {
+    if (count == 0) return;
+    __builtin_amdgcn_s_waitcnt(0);  // earlier stores of this wave have completed
+    for (uint32_t base = 0; base < count; base += 64) {
+      const uint32_t i = base + (uint32_t)lane;
+      if (i < count) {
+        const uint2 e = slots[i];
+        store(act_word_exact(__uint_as_float(e.x), kSilu), e.y);
+      }
+    }
+    count = 0;
+  }
+};
 
 }  // namespace kdaconv
