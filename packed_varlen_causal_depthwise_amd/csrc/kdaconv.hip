@@ -46,10 +46,11 @@ namespace {
 
 constexpr int kWave = 64;
 constexpr int kRows = 16;  // tokens per program
+constexpr int kGroup = 1;  // rows sharing one rare-path branch (divides kRows)
 constexpr int kLaneChannels = 4;  // channels per lane (8-byte vectors)
 constexpr int kMinWaves = 4;  // occupancy target (waves per SIMD)
-// Fixup list entries per wave (8 bytes each in LDS): room for one row of every
-// lane beyond the entries that trigger a flush.
+// Fixup list entries per wave (8 bytes each in LDS): room for one row group of
+// every lane beyond the entries that trigger a flush.
 constexpr int kFixCapacity = 640;
 // Cache-policy bits of buffer loads and stores (gfx950: 1 = sc0, 2 = nt, 16 = sc1).
 constexpr int kStream = 2;  // nontemporal
@@ -112,6 +113,7 @@ struct ConvParams {
   int32_t col_begin;  // first channel of this launch
   int32_t col_end;  // one past its last channel
   int32_t col_blocks;  // column blocks of 64 * kLaneChannels channels in this launch
+  int32_t programs;  // cdiv(num_tokens, kRows) + num_seqs
   int32_t part_dim;
   int32_t search_levels;  // radix-64 levels: smallest L with 64^L >= num_seqs
   int32_t search_top;  // 64^(search_levels - 1)
@@ -161,234 +163,308 @@ __device__ __forceinline__ int find_sequence(const ConvParams& P, int p, int lan
   return base;
 }
 
-template <int V, bool kBias, bool kSilu>
-__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(kMinWaves))) void packed_conv_kernel(const ConvParams P) {
-  static_assert(V % 4 == 0, "the vector weight, bias and state paths take 4 channels at a time");
-  typedef Lane<V> L;
-  typedef typename L::vec vec;
-  const int lane = threadIdx.x;
-  const int p = (int)(blockIdx.x / (uint32_t)P.col_blocks);
-  const int cb = (int)(blockIdx.x - (uint32_t)p * (uint32_t)P.col_blocks);
-  const int c0 = P.col_begin + (cb * kWave + lane) * V;
-  const bool active = c0 < P.col_end;
-  const int cl = active ? c0 : P.col_end - V;  // inactive lanes redo the last active lane
+// One tile: program p of the launch's column block, resolved to its sequence.
+struct Tile {
+  int valid;  // program p covers rows of a sequence
+  int s;  // sequence
+  int j;  // tile index within the sequence
+  int t0;  // first row
+  int n;  // rows (1 .. kRows)
+  int halo;  // 3 history rows precede t0 in x (j > 0), else 0
+  int end;  // one past the sequence's last row
+};
 
+__device__ __forceinline__ Tile describe_tile(const ConvParams& P, int p, int lane) {
+  Tile d{0, 0, 0, 0, 1, 0, 0};
   const int s = find_sequence(P, p, lane);
-  if (s < 0) return;
-
-  // Weights and bias first: vector memory operations complete in issue order, so
-  // loads issued after the x rows could only be used once all the rows had
-  // arrived. 16-byte vectors when the layout allows.
-  float w0[V], w1[V], w2[V], w3[V], bs[V];
-  if (P.weight_vec) {
-    const __amdgpu_buffer_rsrc_t wr = make_rsrc(P.weight);
-#pragma unroll
-    for (int k = 0; k < V; ++k) {
-      const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(wr, (uint32_t)(cl + k) * 16u, 0, kKeep);
-      w0[k] = __uint_as_float(t[0]);
-      w1[k] = __uint_as_float(t[1]);
-      w2[k] = __uint_as_float(t[2]);
-      w3[k] = __uint_as_float(t[3]);
-    }
-  } else {
-#pragma unroll
-    for (int k = 0; k < V; ++k) {
-      const float* wp = P.weight + (int64_t)(cl + k) * P.w_stride0;
-      w0[k] = wp[0];
-      w1[k] = wp[P.w_stride1];
-      w2[k] = wp[2 * P.w_stride1];
-      w3[k] = wp[3 * P.w_stride1];
-    }
-  }
-  if (kBias && P.bias_vec) {
-    const __amdgpu_buffer_rsrc_t br = make_rsrc(P.bias);
-#pragma unroll
-    for (int k = 0; k < V; k += 4) {
-      const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(br, (uint32_t)(cl + k) * 4u, 0, kKeep);
-      bs[k] = __uint_as_float(t[0]);
-      bs[k + 1] = __uint_as_float(t[1]);
-      bs[k + 2] = __uint_as_float(t[2]);
-      bs[k + 3] = __uint_as_float(t[3]);
-    }
-  } else {
-#pragma unroll
-    for (int k = 0; k < V; ++k) bs[k] = kBias ? P.bias[cl + k] : 0.0f;
-  }
-
+  if (s < 0) return d;
   const int T = P.num_tokens;
   const int start = min(max(P.qsl[s], 0), T);
   const int end = min(max(P.qsl[s + 1], start), T);
-  const int len = end - start;
   const int j = p - (s + start / kRows);
-  if ((int64_t)j * kRows >= len) return;  // past the end of its sequence
-  const int t0 = start + j * kRows;
-  const int n = min(kRows, end - t0);
+  if ((int64_t)j * kRows >= end - start) return d;  // past the end of its sequence
+  d.valid = 1;
+  d.s = s;
+  d.j = j;
+  d.t0 = start + j * kRows;
+  d.n = min(kRows, end - d.t0);
+  d.halo = j > 0 ? 3 : 0;
+  d.end = end;
+  return d;
+}
 
-  // History e[t0-3], e[t0-2], e[t0-1]: the stored state for the first tile of a
-  // live sequence with an initial state, zeros for other first tiles (loaded here,
-  // before the x rows), x rows otherwise (below).
-  float h0[V], h1[V], h2[V];
-  bool live = false;
-  int64_t line = 0;
-  if (j == 0) {
-    line = P.cache_indices[(int64_t)s * P.ci_stride];
-    live = !(P.has_null_block && line == P.null_block_id) && line >= 0 &&
-           line < P.num_cache_lines;
-    const bool init = live && P.has_init != nullptr && P.has_init[s] != 0;
-    if (init) {
-      const float* sp = P.states + line * P.cs_stride0;
-      if (P.state_vec) {
-        // The lane's V channels x 3 values are 3V consecutive floats.
-        const __amdgpu_buffer_rsrc_t sr = make_rsrc(sp);
-        float f[3 * V];
+// The per-wave part of the convolution shared by both kernels: the lane's
+// channels, its weights and bias, and the processing of one tile whose x rows
+// were loaded by issue().
+template <int V, bool kBias, bool kSilu>
+struct ConvWorker {
+  typedef Lane<V> L;
+  typedef typename L::vec vec;
+  // x rows of a tile as loaded: 3 history rows, then kRows tile rows.
+  typedef vec Rows[3 + kRows];
+
+  const ConvParams& P;
+  int lane;
+  int cl;  // first channel of the lane (inactive lanes redo the last active lane)
+  bool active;
+  uint32_t xvo, ovo, xrow_bytes, orow_bytes;
+  __amdgpu_buffer_rsrc_t orsrc;  // the launch's output, row 0 of its first plane
+  float w0[V], w1[V], w2[V], w3[V], bs[V];
+  FixupList<kFixCapacity> fix;
+
+  __device__ __forceinline__ ConvWorker(const ConvParams& params, int lane_, int cb, uint2* slots)
+      : P(params), lane(lane_), fix{slots, 0u} {
+    const int c0 = P.col_begin + (cb * kWave + lane) * V;
+    active = c0 < P.col_end;
+    cl = active ? c0 : P.col_end - V;
+    xvo = (uint32_t)(cl * 2);
+    xrow_bytes = (uint32_t)(P.x_row_stride * 2);
+    orow_bytes = (uint32_t)(P.part_dim * 2);
+    const int plane = (cl - P.col_begin) / P.part_dim;
+    const int col = (cl - P.col_begin) - plane * P.part_dim;
+    ovo = (uint32_t)((plane * P.plane_stride + col) * 2);
+    orsrc = make_rsrc(P.out);
+  }
+
+  // Weights and bias: 16-byte vectors when the layout allows. Issued before any x
+  // rows: vector memory operations complete in issue order, so loads issued after
+  // the rows could only be used once all the rows had arrived.
+  __device__ __forceinline__ void load_weights() {
+    if (P.weight_vec) {
+      const __amdgpu_buffer_rsrc_t wr = make_rsrc(P.weight);
 #pragma unroll
-        for (int i = 0; i < 3 * V / 4; ++i) {
-          const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(sr, (uint32_t)cl * 12u + 16u * i, 0, kKeep);
-          f[4 * i] = __uint_as_float(t[0]);
-          f[4 * i + 1] = __uint_as_float(t[1]);
-          f[4 * i + 2] = __uint_as_float(t[2]);
-          f[4 * i + 3] = __uint_as_float(t[3]);
-        }
+      for (int k = 0; k < V; ++k) {
+        const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(wr, (uint32_t)(cl + k) * 16u, 0, kKeep);
+        w0[k] = __uint_as_float(t[0]);
+        w1[k] = __uint_as_float(t[1]);
+        w2[k] = __uint_as_float(t[2]);
+        w3[k] = __uint_as_float(t[3]);
+      }
+    } else {
 #pragma unroll
-        for (int k = 0; k < V; ++k) {
-          h0[k] = f[3 * k];
-          h1[k] = f[3 * k + 1];
-          h2[k] = f[3 * k + 2];
+      for (int k = 0; k < V; ++k) {
+        const float* wp = P.weight + (int64_t)(cl + k) * P.w_stride0;
+        w0[k] = wp[0];
+        w1[k] = wp[P.w_stride1];
+        w2[k] = wp[2 * P.w_stride1];
+        w3[k] = wp[3 * P.w_stride1];
+      }
+    }
+    if (kBias && P.bias_vec) {
+      const __amdgpu_buffer_rsrc_t br = make_rsrc(P.bias);
+#pragma unroll
+      for (int k = 0; k < V; k += 4) {
+        const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(br, (uint32_t)(cl + k) * 4u, 0, kKeep);
+        bs[k] = __uint_as_float(t[0]);
+        bs[k + 1] = __uint_as_float(t[1]);
+        bs[k + 2] = __uint_as_float(t[2]);
+        bs[k + 3] = __uint_as_float(t[3]);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < V; ++k) bs[k] = kBias ? P.bias[cl + k] : 0.0f;
+    }
+  }
+
+  // Issues the loads of a valid tile's x rows: always 3 history rows (the first
+  // row again when the tile has no history) and kRows tile rows (rows past the
+  // tile's end repeat its last row), so the number of loads never depends on the
+  // tile and every load is in bounds. Tile rows are streamed, except the last
+  // three, which the next tile of the column block reads again as its history.
+  __device__ __forceinline__ void issue(Rows& buf, const Tile& d) {
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(P.x + (int64_t)(d.t0 - d.halo) * P.x_row_stride);
+#pragma unroll
+    for (int r = 0; r < 3; ++r)
+      buf[r] = L::template load<kKeep>(xr, xvo, d.halo ? (uint32_t)r * xrow_bytes : 0u);
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+      const uint32_t off = (uint32_t)(min(r, d.n - 1) + d.halo) * xrow_bytes;
+      buf[3 + r] = r < kRows - 3 ? L::template load<kStream>(xr, xvo, off)
+                                 : L::template load<kKeep>(xr, xvo, off);
+    }
+  }
+
+  // Processes a valid tile whose rows issue() loaded into buf.
+  __device__ __forceinline__ void compute(Rows& buf, const Tile& d) {
+    // History e[t0-3], e[t0-2], e[t0-1]: x rows for later tiles; for the first tile
+    // of a sequence the stored state if the sequence is live and has an initial
+    // state, else zeros.
+    float h0[V], h1[V], h2[V];
+    bool live = false;
+    int64_t line = 0;
+    if (d.halo) {
+      unpack<V>(buf[0], h0);
+      unpack<V>(buf[1], h1);
+      unpack<V>(buf[2], h2);
+    } else {
+      line = P.cache_indices[(int64_t)d.s * P.ci_stride];
+      live = !(P.has_null_block && line == P.null_block_id) && line >= 0 &&
+             line < P.num_cache_lines;
+      const bool init = live && P.has_init != nullptr && P.has_init[d.s] != 0;
+      if (init) {
+        const float* sp = P.states + line * P.cs_stride0;
+        if (P.state_vec) {
+          // The lane's V channels x 3 values are 3V consecutive floats.
+          const __amdgpu_buffer_rsrc_t sr = make_rsrc(sp);
+          float f[3 * V];
+#pragma unroll
+          for (int i = 0; i < 3 * V / 4; ++i) {
+            const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(sr, (uint32_t)cl * 12u + 16u * i, 0, kKeep);
+            f[4 * i] = __uint_as_float(t[0]);
+            f[4 * i + 1] = __uint_as_float(t[1]);
+            f[4 * i + 2] = __uint_as_float(t[2]);
+            f[4 * i + 3] = __uint_as_float(t[3]);
+          }
+#pragma unroll
+          for (int k = 0; k < V; ++k) {
+            h0[k] = f[3 * k];
+            h1[k] = f[3 * k + 1];
+            h2[k] = f[3 * k + 2];
+          }
+        } else {
+#pragma unroll
+          for (int k = 0; k < V; ++k) {
+            const float* cp = sp + (int64_t)(cl + k) * P.cs_stride1;
+            h0[k] = cp[0];
+            h1[k] = cp[P.cs_stride2];
+            h2[k] = cp[2 * P.cs_stride2];
+          }
         }
       } else {
 #pragma unroll
+        for (int k = 0; k < V; ++k) h0[k] = h1[k] = h2[k] = 0.0f;
+      }
+    }
+
+    auto fix_store = [&](uint32_t word, uint32_t offset) __attribute__((always_inline)) {
+      __builtin_amdgcn_raw_buffer_store_b16((uint16_t)word, orsrc, offset, 0, kStream);
+    };
+
+    // Rows r0 .. r0 + kGroup - 1 of the tile, of which the first `rows` exist:
+    // taps, activation, stores, history shift. The rows share one rare-path
+    // branch, so their independent arithmetic can interleave.
+    auto group = [&](int r0, int rows) __attribute__((always_inline)) {
+      float acc[kGroup][V];
+#pragma unroll
+      for (int g = 0; g < kGroup; ++g) {
+        float xv[V];
+        unpack<V>(buf[3 + r0 + g], xv);
+#pragma unroll
         for (int k = 0; k < V; ++k) {
-          const float* cp = sp + (int64_t)(cl + k) * P.cs_stride1;
-          h0[k] = cp[0];
-          h1[k] = cp[P.cs_stride2];
-          h2[k] = cp[2 * P.cs_stride2];
+          float a = bs[k];
+          a = __builtin_fmaf(w0[k], h0[k], a);
+          a = __builtin_fmaf(w1[k], h1[k], a);
+          a = __builtin_fmaf(w2[k], h2[k], a);
+          a = __builtin_fmaf(w3[k], xv[k], a);
+          acc[g][k] = a;
+        }
+        if (g < rows) {
+#pragma unroll
+          for (int k = 0; k < V; ++k) {
+            h0[k] = h1[k];
+            h1[k] = h2[k];
+            h2[k] = xv[k];
+          }
         }
       }
+      uint32_t words[kGroup][V / 2];
+      float y[kGroup][V];
+      const bool check = activate_rows<kSilu, V, kGroup>(acc, y, words);
+#pragma unroll
+      for (int g = 0; g < kGroup; ++g) {
+        if (g < rows) {
+          vec o;
+#pragma unroll
+          for (int i = 0; i < V / 2; ++i) o[i] = words[g][i];
+          L::template store<kStream>(o, orsrc, ovo, (uint32_t)(d.t0 + r0 + g) * orow_bytes);
+        }
+      }
+      // Rare (any lane): record the elements whose fast word may be wrong; they
+      // are rewritten when the list is flushed.
+      if (__builtin_expect(__builtin_amdgcn_ballot_w64(check) != 0, 0)) {
+        if (!fix.fits(kGroup * V * kWave)) fix.template flush<kSilu>(lane, fix_store);
+#pragma unroll
+        for (int g = 0; g < kGroup; ++g) {
+          if (g < rows) {
+#pragma unroll
+            for (int k = 0; k < V; ++k)
+              fix.append(needs_exact<kSilu>(acc[g][k], y[g][k]), acc[g][k],
+                         ovo + 2u * k + (uint32_t)(d.t0 + r0 + g) * orow_bytes);
+          }
+        }
+      }
+    };
+    if (d.n == kRows) {
+      // Full tile: straight-line code, no conditions.
+#pragma unroll
+      for (int r0 = 0; r0 < kRows; r0 += kGroup) group(r0, kGroup);
     } else {
 #pragma unroll
-      for (int k = 0; k < V; ++k) h0[k] = h1[k] = h2[k] = 0.0f;
+      for (int r0 = 0; r0 < kRows; r0 += kGroup)
+        if (r0 < d.n) group(r0, min(kGroup, d.n - r0));
+    }
+
+    // Updated state: the last three values of (history ++ x) for this sequence,
+    // written by the sequence's first tile after its reads.
+    if (d.j == 0 && live && active) {
+      if (d.t0 + d.n < d.end) {
+        // The sequence continues past this tile: its last rows are end-3 .. end-1.
+        const __amdgpu_buffer_rsrc_t tr = make_rsrc(P.x + (int64_t)(d.end - 3) * P.x_row_stride);
+        unpack<V>(L::template load<kKeep>(tr, xvo, 0), h0);
+        unpack<V>(L::template load<kKeep>(tr, xvo, xrow_bytes), h1);
+        unpack<V>(L::template load<kKeep>(tr, xvo, 2 * xrow_bytes), h2);
+      }
+      float* sp = P.states + line * P.cs_stride0;
+      if (P.state_vec) {
+        float f[3 * V];
+#pragma unroll
+        for (int k = 0; k < V; ++k) {
+          f[3 * k] = h0[k];
+          f[3 * k + 1] = h1[k];
+          f[3 * k + 2] = h2[k];
+        }
+        float4* sv = reinterpret_cast<float4*>(sp + (int64_t)cl * 3);
+#pragma unroll
+        for (int i = 0; i < 3 * V / 4; ++i)
+          sv[i] = make_float4(f[4 * i], f[4 * i + 1], f[4 * i + 2], f[4 * i + 3]);
+      } else {
+#pragma unroll
+        for (int k = 0; k < V; ++k) {
+          float* cp = sp + (int64_t)(cl + k) * P.cs_stride1;
+          cp[0] = h0[k];
+          cp[P.cs_stride2] = h1[k];
+          cp[2 * P.cs_stride2] = h2[k];
+        }
+      }
     }
   }
 
-
-  // x descriptor based at row t0 - 3 (later tiles read 3 history rows) or t0.
-  const int halo = j > 0 ? 3 : 0;
-  const uint32_t xrow_bytes = (uint32_t)(P.x_row_stride * 2);
-  const __amdgpu_buffer_rsrc_t xr = make_rsrc(P.x + (int64_t)(t0 - halo) * P.x_row_stride);
-  const uint32_t xvo = (uint32_t)(cl * 2);
-
-  // All loads of x first: the history rows, then the tile rows (rows past the
-  // tile's end repeat its last row, so every load is in bounds).
-  vec hraw[3];
-  if (halo) {
-#pragma unroll
-    for (int r = 0; r < 3; ++r) hraw[r] = L::template load<kKeep>(xr, xvo, (uint32_t)r * xrow_bytes);
+  // Rewrites the recorded elements with their exact words.
+  __device__ __forceinline__ void finish() {
+    auto fix_store = [&](uint32_t word, uint32_t offset) __attribute__((always_inline)) {
+      __builtin_amdgcn_raw_buffer_store_b16((uint16_t)word, orsrc, offset, 0, kStream);
+    };
+    fix.template flush<kSilu>(lane, fix_store);
   }
-  vec q[kRows];
-#pragma unroll
-  for (int r = 0; r < kRows; ++r) {
-    const uint32_t off = (uint32_t)(min(r, n - 1) + halo) * xrow_bytes;
-    q[r] = r < kRows - 3 ? L::template load<kStream>(xr, xvo, off) : L::template load<kKeep>(xr, xvo, off);
-  }
+};
 
-  if (halo) {
-    unpack<V>(hraw[0], h0);
-    unpack<V>(hraw[1], h1);
-    unpack<V>(hraw[2], h2);
-  }
-
-  // out descriptor based at row t0 of the launch's first plane; the lane's
-  // plane and column go into its fixed offset.
-  const int plane = (cl - P.col_begin) / P.part_dim;
-  const int col = (cl - P.col_begin) - plane * P.part_dim;
-  const uint32_t orow_bytes = (uint32_t)(P.part_dim * 2);
-  const __amdgpu_buffer_rsrc_t orsrc = make_rsrc(P.out + (int64_t)t0 * P.part_dim);
-  const uint32_t ovo = (uint32_t)((plane * P.plane_stride + col) * 2);
-
-  // Elements needing the exact path, rewritten in batches (FixupList).
+// One wave per tile: the launch is one-dimensional with the column block varying
+// fastest, so waves dispatched together cover whole rows.
+template <int V, bool kBias, bool kSilu>
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(kMinWaves))) void packed_conv_kernel(const ConvParams P) {
+  static_assert(V % 4 == 0, "the vector weight, bias and state paths take 4 channels at a time");
+  const int lane = threadIdx.x;
+  const int p = (int)(blockIdx.x / (uint32_t)P.col_blocks);
+  const int cb = (int)(blockIdx.x - (uint32_t)p * (uint32_t)P.col_blocks);
+  const Tile d = describe_tile(P, p, lane);
+  if (!d.valid) return;
   __shared__ uint2 fix_slots[kFixCapacity];
-  FixupList<kFixCapacity> fix{fix_slots, 0u};
-  auto fix_store = [&](uint32_t word, uint32_t offset) {
-    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)word, orsrc, offset, 0, kStream);
-  };
-
-  // Row r of the tile: taps, activation, store, history shift.
-  auto row = [&](int r) {
-    float xv[V];
-    unpack<V>(q[r], xv);
-    float acc[1][V];
-#pragma unroll
-    for (int k = 0; k < V; ++k) {
-      float a = bs[k];
-      a = __builtin_fmaf(w0[k], h0[k], a);
-      a = __builtin_fmaf(w1[k], h1[k], a);
-      a = __builtin_fmaf(w2[k], h2[k], a);
-      a = __builtin_fmaf(w3[k], xv[k], a);
-      acc[0][k] = a;
-      h0[k] = h1[k];
-      h1[k] = h2[k];
-      h2[k] = xv[k];
-    }
-    uint32_t words[1][V / 2];
-    float y[1][V];
-    const bool check = activate_rows<kSilu, V, 1>(acc, y, words);
-    vec o;
-#pragma unroll
-    for (int i = 0; i < V / 2; ++i) o[i] = words[0][i];
-    L::template store<kStream>(o, orsrc, ovo, (uint32_t)r * orow_bytes);
-    // Rare (any lane): record the elements whose fast word may be wrong; they are
-    // rewritten when the list is flushed.
-    if (__builtin_expect(__builtin_amdgcn_ballot_w64(check) != 0, 0)) {
-      if (!fix.fits(V * kWave)) fix.template flush<kSilu>(lane, fix_store);
-#pragma unroll
-      for (int k = 0; k < V; ++k)
-        fix.append(needs_exact<kSilu>(acc[0][k], y[0][k]), acc[0][k],
-                   ovo + 2u * k + (uint32_t)r * orow_bytes);
-    }
-  };
-  if (n == kRows) {
-    // Full tile: straight-line code, no conditions.
-#pragma unroll
-    for (int r = 0; r < kRows; ++r) row(r);
-  } else {
-#pragma unroll
-    for (int r = 0; r < kRows; ++r)
-      if (r < n) row(r);
-  }
-  fix.template flush<kSilu>(lane, fix_store);
-
-  // Updated state: the last three values of (history ++ x) for this sequence.
-  if (j == 0 && live && active) {
-    if (t0 + n < end) {
-      // The sequence continues past this tile: its last rows are end-3 .. end-1.
-      const __amdgpu_buffer_rsrc_t tr = make_rsrc(P.x + (int64_t)(end - 3) * P.x_row_stride);
-      unpack<V>(L::template load<kKeep>(tr, xvo, 0), h0);
-      unpack<V>(L::template load<kKeep>(tr, xvo, xrow_bytes), h1);
-      unpack<V>(L::template load<kKeep>(tr, xvo, 2 * xrow_bytes), h2);
-    }
-    float* sp = P.states + line * P.cs_stride0;
-    if (P.state_vec) {
-      float f[3 * V];
-#pragma unroll
-      for (int k = 0; k < V; ++k) {
-        f[3 * k] = h0[k];
-        f[3 * k + 1] = h1[k];
-        f[3 * k + 2] = h2[k];
-      }
-      float4* sv = reinterpret_cast<float4*>(sp + (int64_t)cl * 3);
-#pragma unroll
-      for (int i = 0; i < 3 * V / 4; ++i)
-        sv[i] = make_float4(f[4 * i], f[4 * i + 1], f[4 * i + 2], f[4 * i + 3]);
-    } else {
-#pragma unroll
-      for (int k = 0; k < V; ++k) {
-        float* cp = sp + (int64_t)(cl + k) * P.cs_stride1;
-        cp[0] = h0[k];
-        cp[P.cs_stride2] = h1[k];
-        cp[2 * P.cs_stride2] = h2[k];
-      }
-    }
-  }
+  ConvWorker<V, kBias, kSilu> w(P, lane, cb, fix_slots);
+  w.load_weights();
+  typename ConvWorker<V, kBias, kSilu>::Rows buf;
+  w.issue(buf, d);
+  w.compute(buf, d);
+  w.finish();
 }
 
 // The activation map on consecutive FP32 bit patterns, 8 per lane as two rows of 4,
@@ -413,7 +489,7 @@ __global__ __launch_bounds__(kWave) void activation_map_kernel(uint32_t first, u
   __shared__ uint2 fix_slots[kFixCapacity];
   FixupList<kFixCapacity> fix{fix_slots, 0u};
   uint16_t* const block_out = out + block_first;
-  auto fix_store = [&](uint32_t word, uint32_t offset) { block_out[offset] = (uint16_t)word; };
+  auto fix_store = [&](uint32_t word, uint32_t offset) __attribute__((always_inline)) { block_out[offset] = (uint16_t)word; };
   if (__builtin_amdgcn_ballot_w64(check) != 0) {
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
@@ -457,8 +533,8 @@ int validate(const void* x, int64_t num_tokens, int64_t dim, int64_t x_row_strid
 template <int V>
 void launch(ConvParams P, int64_t cols, bool bias, bool silu, hipStream_t st) {
   P.col_blocks = (int32_t)((cols / V + kWave - 1) / kWave);
-  const uint64_t programs = (uint64_t)(P.num_tokens + kRows - 1) / kRows + (uint64_t)P.num_seqs;
-  const dim3 grid((unsigned)(programs * (uint64_t)P.col_blocks));
+  P.programs = (int32_t)((P.num_tokens + kRows - 1) / kRows + P.num_seqs);
+  const dim3 grid((unsigned)((uint64_t)P.programs * (uint64_t)P.col_blocks));
   const dim3 block(kWave);
   if (bias) {
     if (silu)
