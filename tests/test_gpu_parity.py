@@ -68,7 +68,7 @@ def test_dim_not_a_multiple_of_the_wave_width():
     _compare(wl)
 
 
-@pytest.mark.parametrize("parts,part_dim", [(3, 200), (5, 40), (3, 192)])
+@pytest.mark.parametrize("parts,part_dim", [(3, 200), (5, 40), (3, 192), (4, 112)])
 def test_partial_last_column_block_with_states(parts, part_dim):
     """Several column blocks, the last one partial, every sequence starting from its
     stored state: lanes past the last channel must not disturb other lanes' outputs."""
@@ -76,6 +76,23 @@ def test_partial_last_column_block_with_states(parts, part_dim):
 
     wl = make_workload([1, 2, 3, 4, 70, 2], dim=parts * part_dim, part_dim=part_dim, seed=parts,
                        init=[True] * 6, lines=8, activation=None, bias=False)
+    _compare(wl)
+
+
+@pytest.mark.parametrize("activation", ["silu", None])
+def test_tiles_full_of_non_finite_inputs(activation):
+    """Rows of NaN and infinity make every element of their tiles need the exact
+    path, far more than a wave's fixup list holds: those tiles recompute their words
+    themselves. Outputs and states must still match the oracle word for word."""
+    from helpers import make_workload
+
+    wl = make_workload([40, 17, 70], dim=3 * 256, part_dim=256, seed=41, row_stride=768 + 64,
+                       init=[True, False, True], activation=activation)
+    specials = np.array([0x7FC0, 0xFFC1, 0x7F80, 0xFF80, 0x7F81], dtype=np.uint16)
+    rng = np.random.default_rng(41)
+    for r0, r1 in ((4, 30), (45, 50), (90, 127)):
+        block = wl.x[r0:r1, : wl.dim]
+        block[...] = specials[rng.integers(0, len(specials), size=block.shape)]
     _compare(wl)
 
 
