@@ -140,27 +140,44 @@ __device__ __forceinline__ void unpack(typename Lane<V>::vec v, float (&f)[V]) {
   }
 }
 
-// Largest s in [0, num_seqs) with s + floor(qsl[s] / kRows) <= p, or -1.
-// v(s) is strictly increasing for a non-decreasing qsl, so at each level the
-// lanes whose candidate passes form a prefix of the wave.
-__device__ __forceinline__ int find_sequence(const ConvParams& P, int p, int lane) {
+// Sequence s of program p and its raw bounds qsl[s], qsl[s + 1]; s = -1 if none.
+struct SeqBounds {
+  int s;
+  int q0;
+  int q1;
+};
+
+// Largest s in [0, num_seqs) with s + floor(qsl[s] / kRows) <= p, with qsl[s] and
+// qsl[s + 1]. v(s) is strictly increasing for a non-decreasing qsl, so at each level
+// the lanes whose candidate passes form a prefix of the wave. The last level reads
+// consecutive entries, so the bounds are taken from its lanes rather than loaded
+// again: a wave's loads of x wait on one round trip to qsl per level.
+__device__ __forceinline__ SeqBounds find_sequence(const ConvParams& P, int p, int lane) {
+  if (P.search_levels == 0) {
+    // One sequence: both bounds in one round trip.
+    const int q0 = P.qsl[0];
+    const int q1 = P.qsl[1];
+    if (max(q0, 0) / kRows > p) return SeqBounds{-1, 0, 0};
+    return SeqBounds{0, q0, q1};
+  }
   int base = 0;
   int stride = P.search_top;
+  int q = 0;
+  int cnt = 0;
   for (int level = 0; level < P.search_levels; ++level) {
     const int idx = base + lane * stride;
-    bool ok = false;
-    if (idx < P.num_seqs) {
-      const int q = max(P.qsl[idx], 0);
-      ok = idx + q / kRows <= p;
-    }
+    q = idx <= P.num_seqs ? P.qsl[idx] : 0;  // qsl has num_seqs + 1 entries
+    const bool ok = idx < P.num_seqs && idx + max(q, 0) / kRows <= p;
     const uint64_t m = __ballot(ok);
-    const int cnt = __popcll(m);
-    if (cnt == 0) return -1;
+    cnt = __popcll(m);
+    if (cnt == 0) return SeqBounds{-1, 0, 0};
     base += (cnt - 1) * stride;
     stride /= kWave;
   }
-  if (P.search_levels == 0 && max(P.qsl[0], 0) / kRows > p) return -1;
-  return base;
+  // The last level had stride 1: lane cnt - 1 read qsl[base], lane cnt qsl[base + 1].
+  const int q0 = __builtin_amdgcn_readlane(q, cnt - 1);
+  const int q1 = cnt < kWave ? __builtin_amdgcn_readlane(q, cnt) : P.qsl[base + 1];
+  return SeqBounds{base, q0, q1};
 }
 
 // One tile: program p of the launch's column block, resolved to its sequence.
@@ -176,15 +193,15 @@ struct Tile {
 
 __device__ __forceinline__ Tile describe_tile(const ConvParams& P, int p, int lane) {
   Tile d{0, 0, 0, 0, 1, 0, 0};
-  const int s = find_sequence(P, p, lane);
-  if (s < 0) return d;
+  const SeqBounds b = find_sequence(P, p, lane);
+  if (b.s < 0) return d;
   const int T = P.num_tokens;
-  const int start = min(max(P.qsl[s], 0), T);
-  const int end = min(max(P.qsl[s + 1], start), T);
-  const int j = p - (s + start / kRows);
+  const int start = min(max(b.q0, 0), T);
+  const int end = min(max(b.q1, start), T);
+  const int j = p - (b.s + start / kRows);
   if ((int64_t)j * kRows >= end - start) return d;  // past the end of its sequence
   d.valid = 1;
-  d.s = s;
+  d.s = b.s;
   d.j = j;
   d.t0 = start + j * kRows;
   d.n = min(kRows, end - d.t0);
@@ -460,11 +477,12 @@ __global__ __launch_bounds__(kWave * kG) __attribute__((amdgpu_waves_per_eu(kMin
   const int p = (int)(blockIdx.x / groups);
   const int cb = (int)(blockIdx.x - (uint32_t)p * groups) * kG + wave;
   if (cb >= P.col_blocks) return;
-  const Tile d = describe_tile(P, p, lane);
-  if (!d.valid) return;
+  // Weights first: their loads overlap the search for the tile's sequence.
   __shared__ uint2 fix_slots[kG][kFixCapacity];
   ConvWorker<V, kBias, kSilu> w(P, lane, cb, fix_slots[wave]);
   w.load_weights();
+  const Tile d = describe_tile(P, p, lane);
+  if (!d.valid) return;
   typename ConvWorker<V, kBias, kSilu>::Rows buf;
   w.issue(buf, d);
   w.compute(buf, d);
