@@ -11,7 +11,7 @@ the page "vllm.models.kimi_k3.nvidia.ops.kda_conv" is silent, are stated in the
 C file's header.
 
 Pins (tests/test_oracle_*.py): exhaustive bf16 rounding against torch's CPU
-conversion; the correctly rounded exp against mpmath; the SiLU map against exact
+conversion; fp16 rounding and widening against numpy's float16; the correctly rounded exp against mpmath; the SiLU map against exact
 rational arithmetic; the conv against exact-rational brute force, hand-derived
 golden cases, invariants, and PyTorch's float64 conv1d within its error bound.
 """
@@ -64,11 +64,25 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_act_bf16_range.restype = None
     lib.oracle_act_bf16_list.argtypes = [vp, ctypes.c_uint64, i32, vp]
     lib.oracle_act_bf16_list.restype = None
+    lib.oracle_f16_to_f32.argtypes = [ctypes.c_uint16]
+    lib.oracle_f16_to_f32.restype = f32
+    lib.oracle_f16_to_f32_bits.argtypes = [ctypes.c_uint16]
+    lib.oracle_f16_to_f32_bits.restype = ctypes.c_uint32
+    lib.oracle_f32_to_f16.argtypes = [f32]
+    lib.oracle_f32_to_f16.restype = ctypes.c_uint16
+    lib.oracle_f32_word.argtypes = [f32]
+    lib.oracle_f32_word.restype = ctypes.c_uint32
+    lib.oracle_act_word.argtypes = [f32, i32, i32]
+    lib.oracle_act_word.restype = ctypes.c_uint32
+    lib.oracle_act_word_range.argtypes = [ctypes.c_uint32, ctypes.c_uint64, i32, i32, vp]
+    lib.oracle_act_word_range.restype = None
+    lib.oracle_act_word_list.argtypes = [vp, ctypes.c_uint64, i32, i32, vp]
+    lib.oracle_act_word_list.restype = None
     lib.oracle_crexpf_scan.argtypes = [ctypes.c_uint32, ctypes.c_uint64, vp, ctypes.c_uint64,
                                        ctypes.POINTER(ctypes.c_double)]
     lib.oracle_crexpf_scan.restype = ctypes.c_uint64
     lib.oracle_packed_causal_conv1d.argtypes = [
-        vp, i64, i64, i64,  # x, num_tokens, dim, x_row_stride
+        vp, i32, i64, i64, i64,  # x, format, num_tokens, dim, x_row_stride
         vp, i64, i64, vp,  # weight, w_stride0, w_stride1, bias
         vp, i64, i64, i64, i64,  # conv_states, lines, strides
         vp, i64,  # query_start_loc, num_seqs
@@ -90,6 +104,12 @@ def load(path: Optional[pathlib.Path] = None) -> ctypes.CDLL:
             build()
         _lib = _bind(ctypes.CDLL(str(LIBRARY)))
     return _lib
+
+
+#: Element formats of x and the output, as the C file numbers them, with the
+#: numpy dtype that carries their raw words.
+FORMATS = {"bf16": 0, "f16": 1, "f32": 2}
+WORD_DTYPE = {"bf16": np.uint16, "f16": np.uint16, "f32": np.uint32}
 
 
 def is_silu(activation) -> bool:
@@ -116,6 +136,26 @@ def act_bf16(a, silu: bool, lib=None) -> np.ndarray:
     return out
 
 
+def act_words(a, silu: bool, fmt: str = "bf16", lib=None) -> np.ndarray:
+    """Stored word (format ``fmt``) for each FP32 accumulator value in ``a``."""
+    lib = lib or load()
+    bits = np.ascontiguousarray(np.asarray(a, dtype=np.float32).ravel()).view(np.uint32)
+    out = np.empty(bits.size, dtype=WORD_DTYPE[fmt])
+    lib.oracle_act_word_list(bits.ctypes.data, bits.size, int(silu), FORMATS[fmt], out.ctypes.data)
+    return out
+
+
+def act_words_range(first: int, count: int, silu: bool, fmt: str = "bf16", lib=None,
+                    out: Optional[np.ndarray] = None) -> np.ndarray:
+    """Stored words (format ``fmt``) for the FP32 bit patterns first .. first+count-1."""
+    lib = lib or load()
+    if out is None:
+        out = np.empty(count, dtype=WORD_DTYPE[fmt])
+    assert out.dtype == WORD_DTYPE[fmt] and out.flags.c_contiguous and out.size >= count
+    lib.oracle_act_word_range(first & 0xFFFFFFFF, count, int(silu), FORMATS[fmt], out.ctypes.data)
+    return out
+
+
 def act_bf16_range(first: int, count: int, silu: bool, lib=None,
                    out: Optional[np.ndarray] = None) -> np.ndarray:
     """Stored bf16 word for the FP32 bit patterns first, first+1, ..., first+count-1."""
@@ -131,15 +171,20 @@ def packed_causal_conv1d(x: np.ndarray, dim: int, weight: np.ndarray, bias: Opti
                          conv_states: np.ndarray, query_start_loc: np.ndarray,
                          cache_indices: np.ndarray, has_initial_state: Optional[np.ndarray],
                          part_dim: int, activation="silu", null_block_id: Optional[int] = None,
-                         out: Optional[np.ndarray] = None, lib=None) -> np.ndarray:
+                         out: Optional[np.ndarray] = None, lib=None,
+                         x_dtype: str = "bf16") -> np.ndarray:
     """Run the oracle. ``conv_states`` is updated in place; returns ``out``.
 
-    x: uint16 bf16 bits (num_tokens, row_stride) with unit column stride, the op
-    reads columns [0, dim). Returns uint16 (dim // part_dim, num_tokens, part_dim);
-    rows that no sequence owns keep what ``out`` held (zeros when allocated here).
+    x: raw words of format ``x_dtype`` ("bf16" or "f16": uint16, "f32": uint32),
+    shape (num_tokens, row_stride) with unit column stride; the op reads columns
+    [0, dim). Returns words of the same format, (dim // part_dim, num_tokens,
+    part_dim); rows that no sequence owns keep what ``out`` held (zeros when
+    allocated here).
     """
     lib = lib or load()
-    assert x.dtype == np.uint16 and x.ndim == 2 and x.strides[1] == 2
+    wd = WORD_DTYPE[x_dtype]
+    esize = np.dtype(wd).itemsize
+    assert x.dtype == wd and x.ndim == 2 and x.strides[1] == esize
     assert weight.dtype == np.float32 and weight.ndim == 2 and weight.shape == (dim, 4)
     assert conv_states.dtype == np.float32 and conv_states.ndim == 3
     assert conv_states.shape[1] == dim and conv_states.shape[2] == 3
@@ -152,12 +197,12 @@ def packed_causal_conv1d(x: np.ndarray, dim: int, weight: np.ndarray, bias: Opti
         init = np.ascontiguousarray(has_initial_state.astype(np.uint8))
     T = x.shape[0]
     if out is None:
-        out = np.zeros((dim // part_dim, T, part_dim), dtype=np.uint16)
-    assert out.dtype == np.uint16 and out.flags.c_contiguous
+        out = np.zeros((dim // part_dim, T, part_dim), dtype=wd)
+    assert out.dtype == wd and out.flags.c_contiguous
     assert out.shape == (dim // part_dim, T, part_dim)
     S = qsl.shape[0] - 1
     rc = lib.oracle_packed_causal_conv1d(
-        x.ctypes.data, T, dim, x.strides[0] // 2,
+        x.ctypes.data, FORMATS[x_dtype], T, dim, x.strides[0] // esize,
         weight.ctypes.data, weight.strides[0] // 4, weight.strides[1] // 4, _ptr(bias),
         conv_states.ctypes.data, conv_states.shape[0], conv_states.strides[0] // 4,
         conv_states.strides[1] // 4, conv_states.strides[2] // 4,
@@ -174,5 +219,6 @@ def run_workload(wl, out: Optional[np.ndarray] = None, lib=None):
     st = wl.conv_states.copy()
     o = packed_causal_conv1d(wl.x, wl.dim, wl.weight, wl.bias, st, wl.query_start_loc,
                              wl.cache_indices, wl.has_initial_state, wl.part_dim,
-                             wl.activation, wl.null_block_id, out=out, lib=lib)
+                             wl.activation, wl.null_block_id, out=out, lib=lib,
+                             x_dtype=wl.x_dtype)
     return o, st

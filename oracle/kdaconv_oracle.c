@@ -17,7 +17,11 @@
  *     conv_states of shape (cache lines, dim, 3) updated in place, width-4
  *     taps, plane i holds channels [i*part_dim, (i+1)*part_dim);
  *   - packed_causal_conv1d_fn source: activation "silu"/"swish"/True selects
- *     SiLU; a null block id disables the state of the sequences mapped to it.
+ *     SiLU; a null block id disables the state of the sequences mapped to it;
+ *   - packed_causal_conv1d_supported: x may be bf16, fp16 or FP32, the state and
+ *     the weights are FP32, and the output has x's dtype (the function's
+ *     docstring); the arithmetic is FP32 for every input dtype (the note after
+ *     the module docstring: the stock kernel computes in the state dtype).
  *
  * Readings taken where the page is silent (each is listed in the design doc):
  *   - tap 3 multiplies the current token, tap 0 the token three back (causal
@@ -27,7 +31,14 @@
  *     multiply-add per tap, oldest tap first;
  *   - SiLU is a / (1 + exp(-a)) with exp correctly rounded to binary32 and the
  *     add and the divide rounded to binary32 (round to nearest even);
- *   - a NaN result becomes the canonical bf16 quiet NaN 0x7FC0;
+ *   - the output rounds the FP32 result to x's dtype, to nearest even (bf16
+ *     and fp16; an FP32 output is the result itself); fp16 keeps subnormal
+ *     results and overflows to infinity;
+ *   - a NaN result becomes the canonical quiet NaN of the output format:
+ *     0x7FC0 (bf16), 0x7E00 (fp16), 0x7FC00000 (FP32);
+ *   - fp16 -> FP32 widening is the IEEE 754 conversion: exact for every number;
+ *     a NaN keeps its sign and payload and becomes quiet. bf16 -> FP32 and the
+ *     FP32 input keep every bit (the state stores these widened values);
  *   - a sequence whose cache line is the null block runs from zero history and
  *     neither reads nor writes the state; has_initial_state false runs from
  *     zero history and still writes the state;
@@ -70,6 +81,75 @@ uint16_t oracle_f32_to_bf16(float y) {
   uint32_t dropped = u & 0xFFFFu; /* fraction of one bf16 ulp, in 1/65536 */
   if (dropped > 0x8000u || (dropped == 0x8000u && (kept & 1u))) kept += 1;
   return (uint16_t)kept;
+}
+
+/* Element formats of x and of the output (the output takes x's format). */
+#define ORACLE_BF16 0
+#define ORACLE_F16 1
+#define ORACLE_F32 2
+
+/* binary16 -> FP32 (IEEE 754 binary16: sign, 5 exponent bits biased by 15, 10
+ * fraction bits). Numbers widen exactly: a subnormal is fraction * 2^-24, a
+ * normal (1 + fraction / 1024) * 2^(exponent - 15). NaN keeps sign and payload
+ * (fraction moved to the top of the FP32 fraction) and gets the quiet bit. */
+float oracle_f16_to_f32(uint16_t h) {
+  uint32_t sign = (uint32_t)(h >> 15) << 31;
+  uint32_t expo = (h >> 10) & 0x1Fu;
+  uint32_t frac = h & 0x3FFu;
+  if (expo == 0x1Fu) {
+    if (frac == 0) return float_of(sign | 0x7F800000u);
+    return float_of(sign | 0x7FC00000u | (frac << 13));
+  }
+  float mag = expo == 0 ? ldexpf((float)frac, -24) : ldexpf((float)(1024u + frac), (int)expo - 25);
+  return sign ? -mag : mag;
+}
+
+/* oracle_f16_to_f32 as a bit pattern (a float return value passed through a
+ * double would lose a signalling NaN). */
+uint32_t oracle_f16_to_f32_bits(uint16_t h) { return bits_of(oracle_f16_to_f32(h)); }
+
+/* FP32 -> binary16, round to nearest, ties to even. The magnitude is divided by
+ * the binary16 quantum of its binade (2^-24 below 2^-14, where binary16 numbers
+ * are subnormal; 2^(e - 10) in [2^e, 2^(e+1))), an exact scaling by a power of
+ * two, rounded to an integer with rintf (ties to even under the default mode)
+ * and encoded. Magnitudes at or above 65520, the midpoint between the largest
+ * binary16 number 65504 (odd last bit) and 2^16, round to infinity. NaN becomes
+ * the quiet NaN 0x7E00. */
+uint16_t oracle_f32_to_f16(float y) {
+  if (isnan(y)) return 0x7E00;
+  uint16_t sign = signbit(y) ? 0x8000 : 0;
+  float a = fabsf(y);
+  if (a >= 65520.0f) return sign | 0x7C00;
+  if (a < 0x1p-14f) {
+    /* m <= 1024; m == 1024 is 2^-14, the smallest normal, code 0x0400 */
+    uint32_t m = (uint32_t)rintf(a * 0x1p24f);
+    return (uint16_t)(sign | m);
+  }
+  int e;
+  frexpf(a, &e);
+  e -= 1; /* a in [2^e, 2^(e+1)), -14 <= e <= 15 */
+  uint32_t m = (uint32_t)rintf(ldexpf(a, 10 - e)); /* in [1024, 2048] */
+  if (m == 2048) {
+    m = 1024;
+    e += 1;
+  }
+  return (uint16_t)(sign | (uint32_t)((e + 15) << 10) | (m - 1024));
+}
+
+/* The stored FP32 word of an FP32 result: its bits, NaN -> 0x7FC00000. */
+uint32_t oracle_f32_word(float y) { return isnan(y) ? 0x7FC00000u : bits_of(y); }
+
+/* Element of x (format fmt) at index i, widened to FP32. */
+static float load_x(const void* x, int fmt, int64_t i) {
+  if (fmt == ORACLE_F32) return ((const float*)x)[i];
+  uint16_t h = ((const uint16_t*)x)[i];
+  return fmt == ORACLE_F16 ? oracle_f16_to_f32(h) : oracle_bf16_to_f32(h);
+}
+
+/* FP32 result -> stored word of format fmt. */
+static uint32_t store_word(float y, int fmt) {
+  if (fmt == ORACLE_F32) return oracle_f32_word(y);
+  return fmt == ORACLE_F16 ? oracle_f32_to_f16(y) : oracle_f32_to_bf16(y);
 }
 
 /* Midpoint test for the correctly rounded exp below: nonzero when the double
@@ -119,28 +199,52 @@ int oracle_crexpf_escalates(float x) {
   return near_binary32_midpoint(exp((double)x));
 }
 
-/* The map from an FP32 accumulator to the stored bf16 word: SiLU
- * y = a / (1 + exp(-a)) with each operation rounded to binary32 (or y = a when
- * silu == 0), then bf16 rounding. */
-uint16_t oracle_act_bf16(float a, int silu) {
-  float y = a;
-  if (silu) {
-    float e = oracle_crexpf(-a);
-    float d = 1.0f + e;
-    y = a / d;
+/* SiLU y = a / (1 + exp(-a)) with each operation rounded to binary32. */
+static float silu32(float a) {
+  float e = oracle_crexpf(-a);
+  float d = 1.0f + e;
+  return a / d;
+}
+
+/* The map from an FP32 accumulator to the stored word of format fmt: SiLU (or
+ * y = a when silu == 0), then rounding to the format. */
+uint32_t oracle_act_word(float a, int silu, int fmt) {
+  return store_word(silu ? silu32(a) : a, fmt);
+}
+
+/* The same map for the bf16 output. */
+uint16_t oracle_act_bf16(float a, int silu) { return (uint16_t)oracle_act_word(a, silu, ORACLE_BF16); }
+
+/* oracle_act_word over count consecutive FP32 bit patterns starting at first;
+ * out holds uint16 words (bf16, fp16) or uint32 words (FP32). */
+void oracle_act_word_range(uint32_t first, uint64_t count, int silu, int fmt, void* out) {
+  for (uint64_t i = 0; i < count; ++i) {
+    uint32_t w = oracle_act_word(float_of((uint32_t)(first + i)), silu, fmt);
+    if (fmt == ORACLE_F32)
+      ((uint32_t*)out)[i] = w;
+    else
+      ((uint16_t*)out)[i] = (uint16_t)w;
   }
-  return oracle_f32_to_bf16(y);
 }
 
-/* oracle_act_bf16 over count consecutive FP32 bit patterns starting at first. */
+/* oracle_act_word over n FP32 bit patterns given in an array. */
+void oracle_act_word_list(const uint32_t* in, uint64_t n, int silu, int fmt, void* out) {
+  for (uint64_t i = 0; i < n; ++i) {
+    uint32_t w = oracle_act_word(float_of(in[i]), silu, fmt);
+    if (fmt == ORACLE_F32)
+      ((uint32_t*)out)[i] = w;
+    else
+      ((uint16_t*)out)[i] = (uint16_t)w;
+  }
+}
+
+/* bf16 forms of the two above. */
 void oracle_act_bf16_range(uint32_t first, uint64_t count, int silu, uint16_t* out) {
-  for (uint64_t i = 0; i < count; ++i)
-    out[i] = oracle_act_bf16(float_of((uint32_t)(first + i)), silu);
+  oracle_act_word_range(first, count, silu, ORACLE_BF16, out);
 }
 
-/* oracle_act_bf16 over n FP32 bit patterns given in an array. */
 void oracle_act_bf16_list(const uint32_t* in, uint64_t n, int silu, uint16_t* out) {
-  for (uint64_t i = 0; i < n; ++i) out[i] = oracle_act_bf16(float_of(in[i]), silu);
+  oracle_act_word_list(in, n, silu, ORACLE_BF16, out);
 }
 
 /* The FP32 accumulator of one output: bias (or +0.0f), then one fused
@@ -158,7 +262,9 @@ static float conv_acc(const float* w, int64_t ws1, const float* bias_c,
 
 /* The whole operation on host arrays.
  *
- * x:           bf16 bits, row t / channel c at x[t * x_row_stride + c], t < num_tokens.
+ * x:           elements of format fmt (ORACLE_BF16 / ORACLE_F16: uint16 bit
+ *              patterns; ORACLE_F32: float), row t / channel c at
+ *              x[t * x_row_stride + c], t < num_tokens.
  * weight:      FP32, tap k of channel c at weight[c * w_stride0 + k * w_stride1].
  * bias:        FP32 (dim,) or NULL.
  * conv_states: FP32, history k of channel c of line l at
@@ -168,17 +274,19 @@ static float conv_acc(const float* w, int64_t ws1, const float* bias_c,
  * cache_indices:   int32, the line of sequence s at cache_indices[s * ci_stride].
  * has_initial_state: one byte per sequence, nonzero = start from the stored state;
  *                    NULL = no sequence has one.
- * out:         bf16 bits, dense (dim / part_dim, num_tokens, part_dim); rows no
- *              sequence owns are left as they are.
+ * out:         words of format fmt (uint16 for bf16 and fp16, uint32 for FP32),
+ *              dense (dim / part_dim, num_tokens, part_dim); rows no sequence
+ *              owns are left as they are.
  * Returns ORACLE_EINVAL (and writes nothing) for shapes or metadata it cannot
  * give a meaning to; ORACLE_OK otherwise. */
 int oracle_packed_causal_conv1d(
-    const uint16_t* x, int64_t num_tokens, int64_t dim, int64_t x_row_stride,
+    const void* x, int fmt, int64_t num_tokens, int64_t dim, int64_t x_row_stride,
     const float* weight, int64_t w_stride0, int64_t w_stride1, const float* bias,
     float* conv_states, int64_t num_cache_lines, int64_t cs_stride0, int64_t cs_stride1,
     int64_t cs_stride2, const int32_t* query_start_loc, int64_t num_seqs,
     const int32_t* cache_indices, int64_t ci_stride, const uint8_t* has_initial_state,
-    int64_t part_dim, int silu, int has_null_block, int64_t null_block_id, uint16_t* out) {
+    int64_t part_dim, int silu, int has_null_block, int64_t null_block_id, void* out) {
+  if (fmt != ORACLE_BF16 && fmt != ORACLE_F16 && fmt != ORACLE_F32) return ORACLE_EINVAL;
   if (num_tokens < 0 || dim < 0 || num_seqs < 0 || part_dim <= 0 || dim % part_dim != 0)
     return ORACLE_EINVAL;
   if (x_row_stride < dim) return ORACLE_EINVAL;
@@ -208,9 +316,14 @@ int oracle_packed_causal_conv1d(
       int64_t plane = c / part_dim, col = c % part_dim;
       for (int64_t i = 0; i < len; ++i) {
         int64_t t = start + i;
-        float cur = oracle_bf16_to_f32(x[t * x_row_stride + c]);
+        float cur = load_x(x, fmt, t * x_row_stride + c);
         float acc = conv_acc(w, w_stride1, b, hist, cur);
-        out[(plane * num_tokens + t) * part_dim + col] = oracle_act_bf16(acc, silu);
+        uint32_t word = oracle_act_word(acc, silu, fmt);
+        int64_t o = (plane * num_tokens + t) * part_dim + col;
+        if (fmt == ORACLE_F32)
+          ((uint32_t*)out)[o] = word;
+        else
+          ((uint16_t*)out)[o] = (uint16_t)word;
         hist[0] = hist[1];
         hist[1] = hist[2];
         hist[2] = cur;

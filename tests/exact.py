@@ -16,6 +16,7 @@ import mpmath
 
 F32 = (24, -126, 127)  # precision, minimum normal exponent, maximum exponent
 BF16 = (8, -126, 127)
+F16 = (11, -14, 15)
 
 
 def _floor_log2(a: Fraction) -> int:
@@ -147,15 +148,53 @@ def bf16_word(y: float) -> int:
     return bits32(r) >> 16
 
 
-def silu_bf16_word(a: float) -> int:
-    """The stored word for accumulator a: SiLU a / (1 + exp(-a)) in binary32, then bf16."""
+def f16_word(y: float) -> int:
+    """binary16 bit pattern of the binary32 value y rounded to binary16 (NaN -> 0x7E00).
+
+    Rounds the exact rational value to 11 significant bits with binary16's exponent
+    range (subnormals in steps of 2^-24, overflow to infinity); the encoding of the
+    rounded value is struct's "e" format, exact for a representable value."""
+    if math.isnan(y):
+        return 0x7E00
+    if math.isinf(y):
+        return 0xFC00 if y < 0 else 0x7C00
+    r = round_nearest_even(Fraction(y), F16, negative_zero=math.copysign(1.0, y) < 0)
+    if math.isinf(r):
+        return 0xFC00 if r < 0 else 0x7C00
+    return struct.unpack("<H", struct.pack("<e", r))[0]
+
+
+def f32_word(y: float) -> int:
+    """The stored FP32 word of a binary32 value (NaN -> 0x7FC00000)."""
+    return 0x7FC00000 if math.isnan(y) else bits32(y)
+
+
+WORDS = {"bf16": bf16_word, "f16": f16_word, "f32": f32_word}
+
+
+def silu32(a: float) -> float:
+    """SiLU a / (1 + exp(-a)) with exp correctly rounded and each step rounded to binary32."""
     if math.isnan(a):
-        return 0x7FC0
+        return math.nan
     e = exp32(-a)
     d = add32(1.0, e)
-    y = div32(a, d)
-    return bf16_word(y)
+    return div32(a, d)
+
+
+def silu_word(a: float, fmt: str = "bf16") -> int:
+    """The stored word (format fmt) for accumulator a with SiLU."""
+    return WORDS[fmt](silu32(a))
+
+
+def silu_bf16_word(a: float) -> int:
+    """The stored word for accumulator a: SiLU a / (1 + exp(-a)) in binary32, then bf16."""
+    return bf16_word(silu32(a))
 
 
 def bf16_to_float(h: int) -> float:
     return from_bits32((h & 0xFFFF) << 16)
+
+
+def f16_to_float(h: int) -> float:
+    """Value of a binary16 number (not NaN), via struct's "e" format."""
+    return struct.unpack("<e", struct.pack("<H", h & 0xFFFF))[0]

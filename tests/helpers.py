@@ -8,20 +8,22 @@ from typing import Optional
 import numpy as np
 
 import exact
-from workloads import Workload, bf16_bits_to_f32, f32_to_bf16_bits
+from workloads import (CANARIES, WORD_DTYPE, Workload, bf16_bits_to_f32, f32_to_bf16_bits,
+                       f32_to_words, words_to_f32)
 
 
 def make_workload(lengths, dim: int, part_dim: int, *, seed: int = 0, row_stride: Optional[int] = None,
                   lines: Optional[int] = None, init=None, bias: bool = True, activation="silu",
                   null_block_id: Optional[int] = None, cache_indices=None, x_scale: float = 1.0,
-                  pad_tokens: int = 0, state_scale: float = 1.0) -> Workload:
+                  pad_tokens: int = 0, state_scale: float = 1.0, x_dtype: str = "bf16") -> Workload:
     rng = np.random.default_rng(seed)
     lengths = np.asarray(lengths, dtype=np.int64)
     S = len(lengths)
     T = int(lengths.sum()) + pad_tokens
     rs = row_stride or dim
-    x = np.full((T, rs), 0x7FC0, dtype=np.uint16)
-    x[:, :dim] = f32_to_bf16_bits(rng.standard_normal((T, dim)).astype(np.float32) * np.float32(x_scale))
+    x = np.full((T, rs), CANARIES[x_dtype], dtype=WORD_DTYPE[x_dtype])
+    x[:, :dim] = f32_to_words(rng.standard_normal((T, dim)).astype(np.float32) * np.float32(x_scale),
+                              x_dtype)
     w = (rng.standard_normal((dim, 4)) * 0.5).astype(np.float32)
     b = (rng.standard_normal(dim) * 0.1).astype(np.float32) if bias else None
     lines = lines or S + 2
@@ -34,7 +36,8 @@ def make_workload(lengths, dim: int, part_dim: int, *, seed: int = 0, row_stride
     init = np.asarray(init, dtype=bool)
     qsl = np.zeros(S + 1, dtype=np.int32)
     qsl[1:] = np.cumsum(lengths)
-    return Workload("hand", x, dim, w, b, st, qsl, ci, init, part_dim, activation, null_block_id)
+    return Workload("hand", x, dim, w, b, st, qsl, ci, init, part_dim, activation, null_block_id,
+                    x_dtype)
 
 
 def planes_to_rows(out: np.ndarray) -> np.ndarray:
@@ -46,12 +49,13 @@ def planes_to_rows(out: np.ndarray) -> np.ndarray:
 def brute_force(wl: Workload):
     """The operation in exact rational arithmetic with explicit binary32 rounding.
 
-    Returns (out words as (T, dim) uint16, updated conv_states copy). Rows no
-    sequence owns are 0.
+    Returns (out words as (T, dim) in x's format, updated conv_states copy). Rows
+    no sequence owns are 0. Finite x only (the widening is numpy's).
     """
     T, dim = wl.num_tokens, wl.dim
-    xf = bf16_bits_to_f32(wl.x[:, :dim])
-    out = np.zeros((T, dim), dtype=np.uint16)
+    xf = words_to_f32(wl.x[:, :dim], wl.x_dtype)
+    out = np.zeros((T, dim), dtype=WORD_DTYPE[wl.x_dtype])
+    word = exact.WORDS[wl.x_dtype]
     st = wl.conv_states.copy()
     silu = wl.activation in ("silu", "swish", True)
     for s in range(wl.num_seqs):
@@ -68,7 +72,7 @@ def brute_force(wl: Workload):
                 acc = float(wl.bias[c]) if wl.bias is not None else 0.0
                 for k in range(4):
                     acc = exact.fma32(float(wl.weight[c, k]), e[i + k], acc)
-                out[start + i, c] = exact.silu_bf16_word(acc) if silu else exact.bf16_word(acc)
+                out[start + i, c] = word(exact.silu32(acc) if silu else acc)
             if live:
                 st[line, c] = np.array(e[-3:], dtype=np.float32)
     return out, st

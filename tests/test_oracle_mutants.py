@@ -12,6 +12,7 @@ import pytest
 import oracle
 import test_oracle_act as act_pins
 import test_oracle_conv as conv_pins
+import test_oracle_formats as format_pins
 import test_oracle_rounding as round_pins
 
 SRC = oracle.SOURCE.read_text()
@@ -30,7 +31,7 @@ MUTANTS = {
     "unfused multiply-add": [("acc = fmaf(w[1 * ws1], hist[1], acc);",
                               "acc = w[1 * ws1] * hist[1] + acc;")],
     "silu sign": [("oracle_crexpf(-a)", "oracle_crexpf(a)")],
-    "silu via reciprocal": [("y = a / d;", "y = a * (1.0f / d);")],
+    "silu via reciprocal": [("return a / d;", "return a * (1.0f / d);")],
     "state written newest first": [("k * cs_stride2] = hist[k];", "k * cs_stride2] = hist[2 - k];")],
     "state never read": [("int init = live && has_initial_state && has_initial_state[s];",
                           "int init = 0;")],
@@ -38,11 +39,23 @@ MUTANTS = {
                             "int live = 1;\n    int init")],
     "window shift wrong": [("hist[0] = hist[1];\n        hist[1] = hist[2];",
                             "hist[1] = hist[2];\n        hist[0] = hist[1];")],
-    "planes transposed": [("out[(plane * num_tokens + t) * part_dim + col]",
-                           "out[(t * (dim / part_dim) + plane) * part_dim + col]")],
+    "planes transposed": [("int64_t o = (plane * num_tokens + t) * part_dim + col;",
+                           "int64_t o = (t * (dim / part_dim) + plane) * part_dim + col;")],
     "ties away from even": [("(dropped == 0x8000u && (kept & 1u))", "(dropped == 0x8000u)")],
     "bf16 truncates": [("if (dropped > 0x8000u || (dropped == 0x8000u && (kept & 1u))) kept += 1;",
                         "(void)dropped;")],
+    "f16 truncates": [("uint32_t m = (uint32_t)rintf(ldexpf(a, 10 - e));",
+                       "uint32_t m = (uint32_t)truncf(ldexpf(a, 10 - e));")],
+    "f16 subnormal quantum": [("rintf(a * 0x1p24f)", "rintf(a * 0x1p23f)")],
+    "f16 overflow at the largest number": [("if (a >= 65520.0f)", "if (a > 65504.0f)")],
+    "f16 ties away from zero": [("uint32_t m = (uint32_t)rintf(ldexpf(a, 10 - e));",
+                                 "uint32_t m = (uint32_t)roundf(ldexpf(a, 10 - e));")],
+    "f16 widen keeps signalling NaN": [("sign | 0x7FC00000u | (frac << 13)",
+                                        "sign | 0x7F800000u | (frac << 13)")],
+    "f16 widen exponent bias": [("(int)expo - 25", "(int)expo - 24")],
+    "f32 output NaN payload kept": [("isnan(y) ? 0x7FC00000u : bits_of(y)", "bits_of(y)")],
+    "f16 read as bf16": [("return fmt == ORACLE_F16 ? oracle_f16_to_f32(h) : oracle_bf16_to_f32(h);",
+                          "return oracle_bf16_to_f32(h);")],
     "exp one ulp high": [("    return (float)q;\n  }\n  return (float)e;",
                           "    return (float)q;\n  }\n  return nextafterf((float)e, INFINITY);")],
 }
@@ -62,6 +75,11 @@ PINS = [
     ("silu near midpoints", act_pins.test_silu_near_bf16_midpoints),
     ("bf16 closed forms", lambda lib: [round_pins.test_bf16_round_closed_forms(lib, u)
                                        for u in (0x3F808000, 0x3F818000, 0x00018000)]),
+    ("f16 binades", format_pins.test_f16_round_every_binade_critical_bits),
+    ("f16 widen", format_pins.test_f16_widen_every_pattern),
+    ("f32 word", format_pins.test_f32_word_reading),
+    *[(f"brute force {f} {s}", lambda lib, f=f, s=s: format_pins.test_brute_force_exact(lib, f, s))
+      for f in ("f16", "f32") for s in range(3)],
 ]
 
 

@@ -6,8 +6,9 @@ both to the CPU oracle and to the HIP path.
 
 Every array comes from ``numpy.random.Generator(PCG64(seed))`` in a fixed order
 of draws, so a (config, seed) pair gives the same bytes on every host. Float
-inputs are drawn as float32 and rounded to bfloat16 (round to nearest even) by
-the helper below, which is input preparation, not the method.
+inputs are drawn as float32 and rounded to x's format (bfloat16 by the helper
+below, float16 by numpy's conversion, both to nearest even; float32 as drawn),
+which is input preparation, not the method. The x format changes no draw.
 
 Shapes follow the workloads the kda_conv page talks about (vllm.models.kimi_k3.
 nvidia.ops.kda_conv, the ``_config`` comment: 2K-16K tokens x 3 x 1536 packed
@@ -24,6 +25,11 @@ import numpy as np
 
 #: bf16 quiet NaN written into the x columns the op must never read (canary).
 BF16_CANARY = 0x7FC0
+#: The same canary for the other x formats (a quiet NaN of each).
+CANARIES = {"bf16": 0x7FC0, "f16": 0x7E00, "f32": 0x7FC00000}
+#: numpy dtype of the raw words of each x format, and bytes per element.
+WORD_DTYPE = {"bf16": np.uint16, "f16": np.uint16, "f32": np.uint32}
+ELEMENT_BYTES = {"bf16": 2, "f16": 2, "f32": 4}
 
 #: Row stride (elements) of the in_proj output the Q|K|V columns live in.
 IN_PROJ_ROW_STRIDE = 9728
@@ -33,12 +39,14 @@ IN_PROJ_ROW_STRIDE = 9728
 class Workload:
     """One call's worth of host inputs.
 
-    ``x`` is the whole row-strided bf16 buffer, shape ``(num_tokens, row_stride)``,
-    stored as raw uint16 bit patterns; the op reads its first ``dim`` columns.
+    ``x`` is the whole row-strided buffer, shape ``(num_tokens, row_stride)``,
+    stored as raw words of format ``x_dtype`` (uint16 bit patterns for "bf16" and
+    "f16", uint32 for "f32"); the op reads its first ``dim`` columns. The output
+    has the same format.
     """
 
     name: str
-    x: np.ndarray  # uint16 (T, row_stride)
+    x: np.ndarray  # raw words (T, row_stride)
     dim: int
     weight: np.ndarray  # float32 (dim, 4) [channel, tap]
     bias: Optional[np.ndarray]  # float32 (dim,) or None
@@ -49,6 +57,7 @@ class Workload:
     part_dim: int
     activation: Optional[str]  # "silu" or None
     null_block_id: Optional[int]
+    x_dtype: str = "bf16"  # "bf16", "f16" or "f32"
 
     @property
     def num_tokens(self) -> int:
@@ -69,7 +78,8 @@ class Workload:
     def algorithmic_bytes(self) -> int:
         """Bytes the operation must move (no halo re-reads, no slack work).
 
-        x read and out written once (2 B each per element), 12 B of state per
+        x read and out written once (2 B each per element for bf16 and fp16,
+        4 B for FP32), 12 B of state per
         channel read for every sequence that starts from its stored state and
         written for every live non-empty sequence, the weight (16 B per channel),
         the bias (4 B per channel) and the per-sequence metadata.
@@ -82,7 +92,7 @@ class Workload:
         reads_state = live & self.has_initial_state
         writes_state = live & (lens > 0)
         tokens = int(qsl[-1]) if self.num_seqs > 0 else 0
-        b = tokens * self.dim * 2 * 2
+        b = tokens * self.dim * ELEMENT_BYTES[self.x_dtype] * 2
         b += 12 * self.dim * int(reads_state.sum())
         b += 12 * self.dim * int(writes_state.sum())
         b += 16 * self.dim
@@ -104,13 +114,36 @@ def bf16_bits_to_f32(h: np.ndarray) -> np.ndarray:
     return (np.asarray(h, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
+def f32_to_words(a: np.ndarray, x_dtype: str) -> np.ndarray:
+    """Finite float32 values as raw words of ``x_dtype`` (nearest, ties to even)."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    if x_dtype == "bf16":
+        return f32_to_bf16_bits(a)
+    if x_dtype == "f16":
+        return a.astype(np.float16).view(np.uint16)
+    if x_dtype == "f32":
+        return a.view(np.uint32).copy()
+    raise ValueError(f"unknown x format {x_dtype!r}")
+
+
+def words_to_f32(h: np.ndarray, x_dtype: str) -> np.ndarray:
+    """Raw words of ``x_dtype`` widened to float32 (exact for numbers)."""
+    if x_dtype == "bf16":
+        return bf16_bits_to_f32(h)
+    if x_dtype == "f16":
+        return np.asarray(h, dtype=np.uint16).view(np.float16).astype(np.float32)
+    if x_dtype == "f32":
+        return np.asarray(h, dtype=np.uint32).view(np.float32).copy()
+    raise ValueError(f"unknown x format {x_dtype!r}")
+
+
 def _x_buffer(rng: np.random.Generator, tokens: int, dim: int, row_stride: int,
-              scale: float = 1.0) -> np.ndarray:
+              scale: float = 1.0, x_dtype: str = "bf16") -> np.ndarray:
     vals = rng.standard_normal((tokens, dim), dtype=np.float32)
     if scale != 1.0:
         vals *= np.float32(scale)
-    x = np.full((tokens, row_stride), BF16_CANARY, dtype=np.uint16)
-    x[:, :dim] = f32_to_bf16_bits(vals)
+    x = np.full((tokens, row_stride), CANARIES[x_dtype], dtype=WORD_DTYPE[x_dtype])
+    x[:, :dim] = f32_to_words(vals, x_dtype)
     return x
 
 
@@ -124,26 +157,26 @@ def _qsl(lengths: np.ndarray) -> np.ndarray:
     return q.astype(np.int32)
 
 
-def config1(seed: int = 1) -> Workload:
+def config1(seed: int = 1, x_dtype: str = "bf16") -> Workload:
     """1 sequence of 64 tokens, dim 384 as 3 planes of 128, contiguous x, zero state, no init."""
     rng = np.random.Generator(np.random.PCG64(seed))
     T, dim = 64, 384
-    x = _x_buffer(rng, T, dim, dim)
+    x = _x_buffer(rng, T, dim, dim, x_dtype=x_dtype)
     w = _normal(rng, (dim, 4), 0.5)
     b = _normal(rng, (dim,), 0.1)
     st = np.zeros((1, dim, 3), dtype=np.float32)
     return Workload("config1: 1 x 64 tokens, dim 384, part_dim 128", x, dim, w, b, st,
                     _qsl(np.array([T])), np.array([0], dtype=np.int32),
-                    np.array([False]), 128, "silu", None)
+                    np.array([False]), 128, "silu", None, x_dtype)
 
 
-def config2(seed: int = 2) -> Workload:
+def config2(seed: int = 2, x_dtype: str = "bf16") -> Workload:
     """8 sequences of 1-300 tokens, dim 4608 (3 x 1536) in rows of 9728, 4 with initial state."""
     rng = np.random.Generator(np.random.PCG64(seed))
     dim, S, lines = 4608, 8, 64
     lens = rng.integers(1, 300, size=S, endpoint=True)
     T = int(lens.sum())
-    x = _x_buffer(rng, T, dim, IN_PROJ_ROW_STRIDE)
+    x = _x_buffer(rng, T, dim, IN_PROJ_ROW_STRIDE, x_dtype=x_dtype)
     w = _normal(rng, (dim, 4), 0.5)
     b = _normal(rng, (dim,), 0.1)
     st = _normal(rng, (lines, dim, 3), 1.0)
@@ -151,21 +184,21 @@ def config2(seed: int = 2) -> Workload:
     init = np.zeros(S, dtype=bool)
     init[rng.choice(S, size=4, replace=False)] = True
     return Workload("config2: 8 seqs of 1-300 tokens, dim 4608, part_dim 1536, stride 9728",
-                    x, dim, w, b, st, _qsl(lens), ci, init, 1536, "silu", None)
+                    x, dim, w, b, st, _qsl(lens), ci, init, 1536, "silu", None, x_dtype)
 
 
-def config3(seed: int = 3) -> Workload:
+def config3(seed: int = 3, x_dtype: str = "bf16") -> Workload:
     """1 sequence of 16384 tokens, dim 4608 (3 x 1536) in rows of 9728, initial state."""
     rng = np.random.Generator(np.random.PCG64(seed))
     T, dim, lines = 16384, 4608, 8
-    x = _x_buffer(rng, T, dim, IN_PROJ_ROW_STRIDE)
+    x = _x_buffer(rng, T, dim, IN_PROJ_ROW_STRIDE, x_dtype=x_dtype)
     w = _normal(rng, (dim, 4), 0.5)
     b = _normal(rng, (dim,), 0.1)
     st = _normal(rng, (lines, dim, 3), 1.0)
     ci = np.array([rng.integers(lines)], dtype=np.int32)
     return Workload("config3: 1 x 16384 tokens, dim 4608, part_dim 1536, stride 9728",
                     x, dim, w, b, st, _qsl(np.array([T])), ci, np.array([True]), 1536,
-                    "silu", None)
+                    "silu", None, x_dtype)
 
 
 def lognormal_lengths(rng: np.random.Generator, count: int, total: int,
@@ -181,13 +214,13 @@ def lognormal_lengths(rng: np.random.Generator, count: int, total: int,
     return base + 1
 
 
-def config4(seed: int = 4) -> Workload:
+def config4(seed: int = 4, x_dtype: str = "bf16") -> Workload:
     """64 sequences, log-normal lengths plus 1, 2, 3 (16384 tokens), a null-block sequence."""
     rng = np.random.Generator(np.random.PCG64(seed))
     dim, S, lines, T = 4608, 64, 256, 16384
     lens = np.concatenate([lognormal_lengths(rng, S - 3, T - 6), np.array([1, 2, 3])])
     lens = lens[rng.permutation(S)]
-    x = _x_buffer(rng, T, dim, IN_PROJ_ROW_STRIDE)
+    x = _x_buffer(rng, T, dim, IN_PROJ_ROW_STRIDE, x_dtype=x_dtype)
     w = _normal(rng, (dim, 4), 0.5)
     b = _normal(rng, (dim,), 0.1)
     st = _normal(rng, (lines, dim, 3), 1.0)
@@ -199,22 +232,22 @@ def config4(seed: int = 4) -> Workload:
     init = np.zeros(S, dtype=bool)
     init[rng.choice(S, size=48, replace=False)] = True
     return Workload("config4: 64 log-normal seqs (16384 tokens), null block 0, stride 9728",
-                    x, dim, w, b, st, _qsl(lens), ci, init, 1536, "silu", 0)
+                    x, dim, w, b, st, _qsl(lens), ci, init, 1536, "silu", 0, x_dtype)
 
 
-def config5(seed: int = 5) -> Workload:
+def config5(seed: int = 5, x_dtype: str = "bf16") -> Workload:
     """4096 sequences of 1-4 tokens, dim 576 as 3 planes of 192, no bias, no activation."""
     rng = np.random.Generator(np.random.PCG64(seed))
     dim, S, lines = 576, 4096, 8192
     lens = rng.integers(1, 4, size=S, endpoint=True)
     T = int(lens.sum())
-    x = _x_buffer(rng, T, dim, dim)
+    x = _x_buffer(rng, T, dim, dim, x_dtype=x_dtype)
     w = _normal(rng, (dim, 4), 0.5)
     st = _normal(rng, (lines, dim, 3), 1.0)
     ci = rng.permutation(lines)[:S].astype(np.int32)
     init = np.ones(S, dtype=bool)
     return Workload("config5: 4096 seqs of 1-4 tokens, dim 576, part_dim 192, no bias, no act",
-                    x, dim, w, None, st, _qsl(lens), ci, init, 192, None, None)
+                    x, dim, w, None, st, _qsl(lens), ci, init, 192, None, None, x_dtype)
 
 
 CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}
@@ -243,7 +276,7 @@ def random_case(seed: int, *, max_seqs: int = 12, max_len: int = 200, parts: int
         row_pad = int(rng.choice([0, 8, 64, 5136]))
     row_stride = dim + row_pad
     T = int(lens.sum()) + pad_tokens
-    x = _x_buffer(rng, T, dim, row_stride, x_scale)
+    x = _x_buffer(rng, T, dim, row_stride, x_scale, x_dtype)
     w = _normal(rng, (dim, 4), 0.5)
     has_bias = bool(rng.integers(2))
     b = _normal(rng, (dim,), 0.1) if has_bias else None
@@ -255,5 +288,7 @@ def random_case(seed: int, *, max_seqs: int = 12, max_len: int = 200, parts: int
     if bool(rng.integers(2)):
         null_id = int(ci[int(rng.integers(S))])
     act = "silu" if bool(rng.integers(4)) else None
-    return Workload(f"random seed {seed}: S={S} dim={dim} pd={part_dim} stride={row_stride}",
-                    x, dim, w, b, st, _qsl(lens), ci, init, part_dim, act, null_id)
+    fmt = "" if x_dtype == "bf16" else f" x {x_dtype}"
+    return Workload(f"random seed {seed}: S={S} dim={dim} pd={part_dim} stride={row_stride}{fmt}",
+                    x, dim, w, b, st, _qsl(lens), ci, init, part_dim, act,
+                    null_id, x_dtype)
