@@ -4,20 +4,26 @@
  * in_proj output), for AMD Instinct MI355X (gfx950).
  *
  * Operation (page "vllm.models.kimi_k3.nvidia.ops.kda_conv": module docstring,
- * and the packed_causal_conv1d_fn docstring and source):
+ * the packed_causal_conv1d_fn docstring and source, and
+ * packed_causal_conv1d_supported for the admitted dtypes):
  *   For every sequence s, owning rows [qsl[s], qsl[s+1]) of x, and every channel c
  *   of dim = parts * part_dim channels, with e = (3 history values) ++ (the
- *   sequence's bf16 inputs widened to FP32):
+ *   sequence's inputs widened to FP32):
  *     acc  = bias[c] (or +0.0f); then acc = fma(w[c][k], e[t-3+k], acc) for k = 0..3
  *     y    = SiLU(acc) = acc / (1 + exp(-acc)), each step in binary32 (or y = acc)
- *     out[c / part_dim][t][c % part_dim] = y rounded to bf16, to nearest even
+ *     out[c / part_dim][t][c % part_dim] = y in x's format: rounded to bf16 or
+ *            fp16 to nearest even (fp16 keeps subnormals and overflows to
+ *            infinity), or y itself for FP32
  *   The history is conv_states[cache_indices[s]][c][0..2] (index 0 oldest) when
  *   has_initial_state[s] is set, zeros otherwise. After the call that line holds
  *   the last three values of e. A sequence whose line equals null_block_id (when
  *   has_null_block is set) runs from zeros and leaves the states alone. A
  *   zero-length sequence does nothing. The result is bit-identical to a plain
- *   FP32 evaluation of these steps with a correctly rounded exp (NaN results are
- *   stored as 0x7FC0).
+ *   FP32 evaluation of these steps with a correctly rounded exp. NaN results are
+ *   stored as the format's canonical quiet NaN (0x7FC0, 0x7E00, 0x7FC00000).
+ *   bf16 and FP32 inputs widen bit for bit; fp16 inputs widen by the IEEE 754
+ *   conversion (exact for numbers, a signalling NaN becomes quiet). The state
+ *   receives the widened values.
  *
  * Conventions for every entry point:
  *   - Sizes and strides count ELEMENTS, not bytes. Pointers are DEVICE pointers
@@ -58,13 +64,24 @@ typedef enum kdaconv_activation {
   KDACONV_ACT_SILU = 1
 } kdaconv_activation;
 
+/* Element format of x and of the output (the output takes x's format). */
+typedef enum kdaconv_dtype {
+  KDACONV_BF16 = 0,
+  KDACONV_F16 = 1,
+  KDACONV_F32 = 2
+} kdaconv_dtype;
+
 /*
  * The convolution (packed_causal_conv1d_fn on the page named above).
  *
- * x                  bf16 bit patterns; element (t, c) at x[t * x_row_stride + c],
- *                    rows t < num_tokens, channels c < dim. Only columns [0, dim)
- *                    are read. 16-byte aligned; x_row_stride >= dim and a multiple
- *                    of 8 (else EUNSUPPORTED).
+ * x                  elements of format dtype; element (t, c) at
+ *                    x[t * x_row_stride + c], rows t < num_tokens, channels c < dim.
+ *                    Only columns [0, dim) are read. 16-byte aligned;
+ *                    x_row_stride >= dim, and rows a multiple of 16 bytes apart
+ *                    (x_row_stride a multiple of 8 for bf16 and fp16, of 4 for
+ *                    FP32; else EUNSUPPORTED).
+ * dtype              KDACONV_BF16, KDACONV_F16 or KDACONV_F32 (else EINVAL): the
+ *                    format of x and of out.
  * weight             FP32; tap k of channel c at weight[c * weight_stride0 +
  *                    k * weight_stride1] (page layout [channel, width], width 4).
  * bias               FP32 (dim,) contiguous, or NULL for none.
@@ -86,8 +103,9 @@ typedef enum kdaconv_activation {
  * has_null_block,
  * null_block_id      when has_null_block != 0, sequences whose line equals
  *                    null_block_id skip the state (page: HAS_NULL_BLOCK).
- * out                bf16 bit patterns, dense (dim / part_dim, num_tokens, part_dim),
- *                    16-byte aligned. Rows no sequence owns are left unwritten.
+ * out                elements of format dtype, dense (dim / part_dim, num_tokens,
+ *                    part_dim), 16-byte aligned. Rows no sequence owns are left
+ *                    unwritten.
  *
  * Device-data preconditions (not checked; violating them gives unspecified
  * values but no access outside the buffers described above): query_start_loc
@@ -95,7 +113,7 @@ typedef enum kdaconv_activation {
  * num_tokens == 0, num_seqs == 0 or dim == 0 returns KDACONV_OK with no launch.
  */
 int kdaconv_packed_causal_conv1d(
-    const void* x, int64_t num_tokens, int64_t dim, int64_t x_row_stride,
+    const void* x, int dtype, int64_t num_tokens, int64_t dim, int64_t x_row_stride,
     const float* weight, int64_t weight_stride0, int64_t weight_stride1,
     const float* bias,
     float* conv_states, int64_t num_cache_lines,
@@ -113,7 +131,7 @@ int kdaconv_packed_causal_conv1d(
  * dereferenced, so host addresses may stand in for device ones. Makes no HIP call.
  */
 int kdaconv_validate(
-    const void* x, int64_t num_tokens, int64_t dim, int64_t x_row_stride,
+    const void* x, int dtype, int64_t num_tokens, int64_t dim, int64_t x_row_stride,
     const float* weight, int64_t weight_stride0, int64_t weight_stride1,
     const float* bias,
     const float* conv_states, int64_t num_cache_lines,
@@ -125,14 +143,15 @@ int kdaconv_validate(
     const void* out);
 
 /*
- * The device map from an FP32 accumulator to the stored bf16 word, exactly as
- * the convolution kernel applies it (SiLU or none, then bf16 rounding; module
- * docstring of the page named above), evaluated for the `count` FP32 bit
- * patterns first, first + 1, ... (wrapping at 2^32). out: device uint16 array of
- * `count` entries, 16-byte aligned. count must be a multiple of 8 (else EINVAL).
- * Used to check the kernel's activation against a reference on every input.
+ * The device map from an FP32 accumulator to the stored word of format dtype,
+ * exactly as the convolution kernel applies it (SiLU or none, then the format's
+ * rounding; module docstring of the page named above), evaluated for the `count`
+ * FP32 bit patterns first, first + 1, ... (wrapping at 2^32). out: device array of
+ * `count` words (uint16 for bf16 and fp16, uint32 for FP32), 16-byte aligned.
+ * count must be a multiple of 8 (else EINVAL). Used to check the kernel's
+ * activation against a reference on every input.
  */
-int kdaconv_activation_map(uint32_t first, int64_t count, int activation, uint16_t* out,
+int kdaconv_activation_map(uint32_t first, int64_t count, int activation, int dtype, void* out,
                            kdaconv_stream_t stream);
 
 /* Static English text for a status code. Never NULL. */

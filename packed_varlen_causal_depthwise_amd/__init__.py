@@ -43,6 +43,17 @@ def _activation_code(activation) -> int:
     raise ValueError(f"unknown activation {activation!r}: use 'silu', 'swish', True, None or False")
 
 
+# x formats the library takes, with their interface codes (the output takes x's dtype).
+_DTYPE_CODES = {torch.bfloat16: _lib.BF16, torch.float16: _lib.F16, torch.float32: _lib.F32}
+_FORMAT_NAMES = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
+
+
+def _dtype_code(dtype: torch.dtype) -> int:
+    if dtype not in _DTYPE_CODES:
+        raise ValueError(f"x must be bfloat16, float16 or float32 (got {dtype})")
+    return _DTYPE_CODES[dtype]
+
+
 def _stream_handle(device: torch.device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
@@ -56,7 +67,7 @@ def _conv_args(x, weight, bias, conv_states, query_start_loc, cache_indices, has
     num_tokens, dim = x.shape
     num_seqs = query_start_loc.numel() - 1
     return [
-        _ptr(x), num_tokens, dim, x.stride(0),
+        _ptr(x), _dtype_code(x.dtype), num_tokens, dim, x.stride(0),
         _ptr(weight), weight.stride(0), weight.stride(1), _ptr(bias),
         _ptr(conv_states), conv_states.size(0),
         conv_states.stride(0), conv_states.stride(1), conv_states.stride(2),
@@ -72,8 +83,7 @@ def _conv_args(x, weight, bias, conv_states, query_start_loc, cache_indices, has
 def _check_tensors(x, weight, bias, conv_states, query_start_loc, cache_indices, has_initial_state):
     if not x.is_cuda:
         raise ValueError("x must be a GPU tensor")
-    if x.dtype != torch.bfloat16:
-        raise ValueError(f"x must be bfloat16 (got {x.dtype})")
+    _dtype_code(x.dtype)
     if x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be 2-D (tokens, dim) with unit column stride")
     dim = x.size(1)
@@ -120,11 +130,13 @@ def packed_causal_conv1d_fn(
 
     Semantics of page vllm.models.kimi_k3.nvidia.ops.kda_conv,
     packed_causal_conv1d_fn: causal_conv1d_fn(x.T, weight, bias, conv_states, ...).T
-    with conv_states (cache lines, dim, 3) updated in place. Returns
-    (dim // part_dim, tokens, part_dim) bf16; plane i holds channels
-    [i * part_dim, (i + 1) * part_dim). ``out``, when given, must be a contiguous
-    bf16 tensor of that shape and receives the result (rows no sequence owns are
-    left as they were). Queued on the current stream; no synchronisation.
+    with conv_states (cache lines, dim, 3) updated in place. x is bfloat16,
+    float16 or float32 (page: packed_causal_conv1d_supported); the arithmetic is
+    FP32 and the result has x's dtype, (dim // part_dim, tokens, part_dim); plane i
+    holds channels [i * part_dim, (i + 1) * part_dim). ``out``, when given, must be
+    a contiguous tensor of x's dtype and that shape and receives the result (rows
+    no sequence owns are left as they were). Queued on the current stream; no
+    synchronisation.
     """
     if x.dim() != 2:
         raise ValueError("x must be 2-D (tokens, dim)")
@@ -152,11 +164,11 @@ def packed_causal_conv1d_fn(
 def packed_causal_conv1d_supported(x: torch.Tensor, weight: torch.Tensor,
                                    conv_states: torch.Tensor, part_dim: int) -> bool:
     """Whether packed_causal_conv1d_fn serves these tensors (page:
-    packed_causal_conv1d_supported). This build takes bf16 x with unit column
-    stride and a row stride that is a multiple of 8, FP32 weight (dim, 4), FP32
+    packed_causal_conv1d_supported). This build takes bf16, fp16 or FP32 x with
+    unit column stride and rows 16 bytes apart, FP32 weight (dim, 4), FP32
     conv_states (lines, dim, 3), and part_dim a multiple of 8 dividing dim."""
     try:
-        if not (x.is_cuda and x.dim() == 2 and x.stride(1) == 1 and x.dtype == torch.bfloat16):
+        if not (x.is_cuda and x.dim() == 2 and x.stride(1) == 1 and x.dtype in _DTYPE_CODES):
             return False
         if not (weight.dtype == torch.float32 and weight.dim() == 2
                 and tuple(weight.shape) == (x.size(1), 4)):
@@ -172,22 +184,27 @@ def packed_causal_conv1d_supported(x: torch.Tensor, weight: torch.Tensor,
     num_tokens, dim = x.shape
     # The output buffer would be a fresh 256-byte-aligned allocation.
     rc = lib.kdaconv_validate(
-        _ptr(x), num_tokens, dim, x.stride(0), _ptr(weight), weight.stride(0), weight.stride(1),
+        _ptr(x), _DTYPE_CODES[x.dtype], num_tokens, dim, x.stride(0), _ptr(weight), weight.stride(0), weight.stride(1),
         None, _ptr(conv_states), conv_states.size(0), conv_states.stride(0),
         conv_states.stride(1), conv_states.stride(2), 256, 1, 256, 1, None, int(part_dim),
         _lib.ACT_SILU, 0, 0, 256)
     return rc == _lib.OK
 
 
-def activation_map(first: int, count: int, activation, out: Optional[torch.Tensor] = None
-                   ) -> torch.Tensor:
-    """The kernel's FP32 -> stored-bf16-word map on ``count`` consecutive FP32 bit
-    patterns from ``first``; returns an int16 tensor of words on the current device."""
+def activation_map(first: int, count: int, activation, out: Optional[torch.Tensor] = None,
+                   fmt: str = "bf16") -> torch.Tensor:
+    """The kernel's FP32 -> stored-word map (output format ``fmt``: "bf16", "f16" or
+    "f32") on ``count`` consecutive FP32 bit patterns from ``first``; returns the
+    words as an int16 (bf16, f16) or int32 (f32) tensor on the current device."""
+    code = _DTYPE_CODES[_FORMAT_NAMES[fmt]]
+    wdt = torch.int32 if code == _lib.F32 else torch.int16
     if out is None:
-        out = torch.empty(count, dtype=torch.int16, device="cuda")
+        out = torch.empty(count, dtype=wdt, device="cuda")
+    if out.dtype != wdt or not out.is_contiguous() or out.numel() < count:
+        raise ValueError(f"out must be a contiguous {wdt} tensor of at least {count} elements")
     lib = _lib.load()
     with torch.cuda.device(out.device):
         rc = lib.kdaconv_activation_map(first & 0xFFFFFFFF, count, _activation_code(activation),
-                                        out.data_ptr(), _stream_handle(out.device))
+                                        code, out.data_ptr(), _stream_handle(out.device))
     _lib.check(rc, "activation_map")
     return out

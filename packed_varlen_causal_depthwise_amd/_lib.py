@@ -9,6 +9,7 @@ LIBRARY = pathlib.Path(__file__).resolve().parent / "libkdaconv.so"
 
 OK, EINVAL, EUNSUPPORTED, ELAUNCH = 0, 1, 2, 3
 ACT_NONE, ACT_SILU = 0, 1
+BF16, F16, F32 = 0, 1, 2
 
 # Every entry point include/kdaconv.h declares.
 EXPORTS = (
@@ -38,7 +39,7 @@ def load() -> ctypes.CDLL:
     lib = ctypes.CDLL(str(LIBRARY))
     i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
     conv_args = [
-        vp, i64, i64, i64,  # x, num_tokens, dim, x_row_stride
+        vp, i32, i64, i64, i64,  # x, dtype, num_tokens, dim, x_row_stride
         vp, i64, i64, vp,  # weight, weight strides, bias
         vp, i64, i64, i64, i64,  # conv_states, num_cache_lines, strides
         vp, i64,  # query_start_loc, num_seqs
@@ -50,7 +51,7 @@ def load() -> ctypes.CDLL:
     lib.kdaconv_packed_causal_conv1d.restype = i32
     lib.kdaconv_validate.argtypes = conv_args
     lib.kdaconv_validate.restype = i32
-    lib.kdaconv_activation_map.argtypes = [ctypes.c_uint32, i64, i32, vp, vp]
+    lib.kdaconv_activation_map.argtypes = [ctypes.c_uint32, i64, i32, i32, vp, vp]
     lib.kdaconv_activation_map.restype = i32
     lib.kdaconv_status_string.argtypes = [i32]
     lib.kdaconv_status_string.restype = ctypes.c_char_p

@@ -4,15 +4,17 @@
 // packed_causal_conv1d_fn docstring and source; packed_causal_conv1d_supported)
 // defines the operation; include/kdaconv.h states it in full.
 //
-// Work decomposition. A program is one wave64 handling a tile of kRows
-// consecutive tokens of one sequence over 64 * kLaneChannels channels: each lane
-// owns kLaneChannels consecutive channels, so every x row and every output row of
-// the tile moves as one vector per lane. Programs are numbered so that sequence s
-// owns programs v(s) .. v(s+1)-1 with v(s) = s + floor(qsl[s] / kRows); the wave
+// Work decomposition. A program is one wave64 handling a tile of R consecutive
+// tokens of one sequence over 64 * kLaneChannels channels: each lane owns
+// kLaneChannels consecutive channels, so every x row and every output row of the
+// tile moves as one vector per lane (8 bytes for bf16 and fp16, 16 for FP32; R is
+// 16 for the 16-bit formats and 8 for FP32, so a wave's loads in flight stay the
+// same). Programs are numbered so that sequence s owns programs v(s) .. v(s+1)-1
+// with v(s) = s + floor(qsl[s] / R); the wave
 // finds its sequence on the device with a radix-64 search over query_start_loc
-// (one ballot per level), so the grid, cdiv(T, kRows) + num_seqs programs times
+// (one ballot per level), so the grid, cdiv(T, R) + num_seqs programs times
 // the column blocks, depends only on host sizes and the launch can be captured in
-// a graph. Tile j of sequence s covers rows [start + j*kRows, start + (j+1)*kRows)
+// a graph. Tile j of sequence s covers rows [start + j*R, start + (j+1)*R)
 // of the sequence; programs past the end of their sequence exit at once. The
 // launch is one-dimensional with the column block varying fastest, so waves
 // dispatched together cover whole rows; waves are short, and the dispatcher keeps
@@ -45,9 +47,8 @@ namespace kdaconv {
 namespace {
 
 constexpr int kWave = 64;
-constexpr int kRows = 16;  // tokens per program
-constexpr int kGroup = 1;  // rows sharing one rare-path branch (divides kRows)
-constexpr int kLaneChannels = 4;  // channels per lane (8-byte vectors)
+constexpr int kGroup = 1;  // rows sharing one rare-path branch (divides R)
+constexpr int kLaneChannels = 4;  // channels per lane
 constexpr int kMinWaves = 4;  // occupancy target (waves per SIMD)
 // Fixup list entries per wave (8 bytes each in LDS): room for one row group of
 // every lane beyond the entries that trigger a flush.
@@ -61,11 +62,20 @@ constexpr int32_t kRange = 0x7FFFFFFF;
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-template <int V>
+// Tokens per program for each format.
+template <int kF>
+constexpr int rows_per_tile() {
+  return kF == kF32 ? 8 : 16;
+}
+
+int rows_per_tile(int dtype) { return dtype == kF32 ? rows_per_tile<kF32>() : rows_per_tile<kBF16>(); }
+
+// Buffer loads and stores of kBytes per lane.
+template <int kBytes>
 struct Lane;
 
 template <>
-struct Lane<4> {
+struct Lane<8> {
   typedef u32x2 vec;
   template <int kPolicy>
   static __device__ __forceinline__ vec load(__amdgpu_buffer_rsrc_t r, uint32_t vo, uint32_t so) {
@@ -79,7 +89,7 @@ struct Lane<4> {
 };
 
 template <>
-struct Lane<8> {
+struct Lane<16> {
   typedef u32x4 vec;
   template <int kPolicy>
   static __device__ __forceinline__ vec load(__amdgpu_buffer_rsrc_t r, uint32_t vo, uint32_t so) {
@@ -93,14 +103,14 @@ struct Lane<8> {
 };
 
 struct ConvParams {
-  const uint16_t* x;
+  const char* x;
   const float* weight;
   const float* bias;
   float* states;
   const int32_t* __restrict__ qsl;
   const int32_t* __restrict__ cache_indices;
   const uint8_t* __restrict__ has_init;
-  uint16_t* out;  // first plane of this launch
+  char* out;  // first plane of this launch
   int64_t x_row_stride;
   int64_t w_stride0, w_stride1;
   int64_t cs_stride0, cs_stride1, cs_stride2;
@@ -113,7 +123,7 @@ struct ConvParams {
   int32_t col_begin;  // first channel of this launch
   int32_t col_end;  // one past its last channel
   int32_t col_blocks;  // column blocks of 64 * kLaneChannels channels in this launch
-  int32_t programs;  // cdiv(num_tokens, kRows) + num_seqs
+  int32_t programs;  // cdiv(num_tokens, R) + num_seqs
   int32_t part_dim;
   int32_t search_levels;  // radix-64 levels: smallest L with 64^L >= num_seqs
   int32_t search_top;  // 64^(search_levels - 1)
@@ -127,16 +137,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, kRange, kDescWord3);
 }
 
-// The widened values pass through an empty asm statement: the compiler cannot
-// recompute them later from the packed word (rematerialization), which would keep
-// the queue slot's registers alive past the refill load.
-template <int V>
-__device__ __forceinline__ void unpack(typename Lane<V>::vec v, float (&f)[V]) {
+// The lane's V elements of one row, widened to FP32. The widened values pass
+// through an empty asm statement: the compiler cannot recompute them later from the
+// packed word (rematerialization), which would keep the row's registers alive.
+template <int kF, int V>
+__device__ __forceinline__ void unpack(typename Lane<V * element_bytes<kF>()>::vec v, float (&f)[V]) {
+  if (kF == kF32) {
 #pragma unroll
-  for (int i = 0; i < V / 2; ++i) {
-    f[2 * i] = widen_lo(v[i]);
-    f[2 * i + 1] = widen_hi(v[i]);
-    asm volatile("" : "+v"(f[2 * i]), "+v"(f[2 * i + 1]));
+    for (int i = 0; i < V; ++i) f[i] = __uint_as_float(v[i]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < V / 2; ++i) {
+      f[2 * i] = widen_half<kF>(v[i], 0);
+      f[2 * i + 1] = widen_half<kF>(v[i], 1);
+      asm volatile("" : "+v"(f[2 * i]), "+v"(f[2 * i + 1]));
+    }
   }
 }
 
@@ -147,17 +162,18 @@ struct SeqBounds {
   int q1;
 };
 
-// Largest s in [0, num_seqs) with s + floor(qsl[s] / kRows) <= p, with qsl[s] and
+// Largest s in [0, num_seqs) with s + floor(qsl[s] / R) <= p, with qsl[s] and
 // qsl[s + 1]. v(s) is strictly increasing for a non-decreasing qsl, so at each level
 // the lanes whose candidate passes form a prefix of the wave. The last level reads
 // consecutive entries, so the bounds are taken from its lanes rather than loaded
 // again: a wave's loads of x wait on one round trip to qsl per level.
+template <int R>
 __device__ __forceinline__ SeqBounds find_sequence(const ConvParams& P, int p, int lane) {
   if (P.search_levels == 0) {
     // One sequence: both bounds in one round trip.
     const int q0 = P.qsl[0];
     const int q1 = P.qsl[1];
-    if (max(q0, 0) / kRows > p) return SeqBounds{-1, 0, 0};
+    if (max(q0, 0) / R > p) return SeqBounds{-1, 0, 0};
     return SeqBounds{0, q0, q1};
   }
   int base = 0;
@@ -167,7 +183,7 @@ __device__ __forceinline__ SeqBounds find_sequence(const ConvParams& P, int p, i
   for (int level = 0; level < P.search_levels; ++level) {
     const int idx = base + lane * stride;
     q = idx <= P.num_seqs ? P.qsl[idx] : 0;  // qsl has num_seqs + 1 entries
-    const bool ok = idx < P.num_seqs && idx + max(q, 0) / kRows <= p;
+    const bool ok = idx < P.num_seqs && idx + max(q, 0) / R <= p;
     const uint64_t m = __ballot(ok);
     cnt = __popcll(m);
     if (cnt == 0) return SeqBounds{-1, 0, 0};
@@ -186,25 +202,26 @@ struct Tile {
   int s;  // sequence
   int j;  // tile index within the sequence
   int t0;  // first row
-  int n;  // rows (1 .. kRows)
+  int n;  // rows (1 .. R)
   int halo;  // 3 history rows precede t0 in x (j > 0), else 0
   int end;  // one past the sequence's last row
 };
 
+template <int R>
 __device__ __forceinline__ Tile describe_tile(const ConvParams& P, int p, int lane) {
   Tile d{0, 0, 0, 0, 1, 0, 0};
-  const SeqBounds b = find_sequence(P, p, lane);
+  const SeqBounds b = find_sequence<R>(P, p, lane);
   if (b.s < 0) return d;
   const int T = P.num_tokens;
   const int start = min(max(b.q0, 0), T);
   const int end = min(max(b.q1, start), T);
-  const int j = p - (b.s + start / kRows);
-  if ((int64_t)j * kRows >= end - start) return d;  // past the end of its sequence
+  const int j = p - (b.s + start / R);
+  if ((int64_t)j * R >= end - start) return d;  // past the end of its sequence
   d.valid = 1;
   d.s = b.s;
   d.j = j;
-  d.t0 = start + j * kRows;
-  d.n = min(kRows, end - d.t0);
+  d.t0 = start + j * R;
+  d.n = min(R, end - d.t0);
   d.halo = j > 0 ? 3 : 0;
   d.end = end;
   return d;
@@ -213,12 +230,13 @@ __device__ __forceinline__ Tile describe_tile(const ConvParams& P, int p, int la
 // The per-wave part of the convolution shared by both kernels: the lane's
 // channels, its weights and bias, and the processing of one tile whose x rows
 // were loaded by issue().
-template <int V, bool kBias, bool kSilu>
+template <int kF, int V, int R, bool kBias, bool kSilu>
 struct ConvWorker {
-  typedef Lane<V> L;
+  static constexpr int kBytes = element_bytes<kF>();
+  typedef Lane<V * kBytes> L;
   typedef typename L::vec vec;
-  // x rows of a tile as loaded: 3 history rows, then kRows tile rows.
-  typedef vec Rows[3 + kRows];
+  // x rows of a tile as loaded: 3 history rows, then R tile rows.
+  typedef vec Rows[3 + R];
 
   const ConvParams& P;
   int lane;
@@ -234,12 +252,12 @@ struct ConvWorker {
     const int c0 = P.col_begin + (cb * kWave + lane) * V;
     active = c0 < P.col_end;
     cl = active ? c0 : P.col_end - V;
-    xvo = (uint32_t)(cl * 2);
-    xrow_bytes = (uint32_t)(P.x_row_stride * 2);
-    orow_bytes = (uint32_t)(P.part_dim * 2);
+    xvo = (uint32_t)(cl * kBytes);
+    xrow_bytes = (uint32_t)(P.x_row_stride * kBytes);
+    orow_bytes = (uint32_t)(P.part_dim * kBytes);
     const int plane = (cl - P.col_begin) / P.part_dim;
     const int col = (cl - P.col_begin) - plane * P.part_dim;
-    ovo = (uint32_t)((plane * P.plane_stride + col) * 2);
+    ovo = (uint32_t)((plane * P.plane_stride + col) * kBytes);
     orsrc = make_rsrc(P.out);
   }
 
@@ -284,20 +302,21 @@ struct ConvWorker {
   }
 
   // Issues the loads of a valid tile's x rows: always 3 history rows (the first
-  // row again when the tile has no history) and kRows tile rows (rows past the
+  // row again when the tile has no history) and R tile rows (rows past the
   // tile's end repeat its last row), so the number of loads never depends on the
   // tile and every load is in bounds. Tile rows are streamed, except the last
   // three, which the next tile of the column block reads again as its history.
   __device__ __forceinline__ void issue(Rows& buf, const Tile& d) {
-    const __amdgpu_buffer_rsrc_t xr = make_rsrc(P.x + (int64_t)(d.t0 - d.halo) * P.x_row_stride);
+    const __amdgpu_buffer_rsrc_t xr =
+        make_rsrc(P.x + (int64_t)(d.t0 - d.halo) * P.x_row_stride * kBytes);
 #pragma unroll
     for (int r = 0; r < 3; ++r)
       buf[r] = L::template load<kKeep>(xr, xvo, d.halo ? (uint32_t)r * xrow_bytes : 0u);
 #pragma unroll
-    for (int r = 0; r < kRows; ++r) {
+    for (int r = 0; r < R; ++r) {
       const uint32_t off = (uint32_t)(min(r, d.n - 1) + d.halo) * xrow_bytes;
-      buf[3 + r] = r < kRows - 3 ? L::template load<kStream>(xr, xvo, off)
-                                 : L::template load<kKeep>(xr, xvo, off);
+      buf[3 + r] = r < R - 3 ? L::template load<kStream>(xr, xvo, off)
+                             : L::template load<kKeep>(xr, xvo, off);
     }
   }
 
@@ -310,9 +329,9 @@ struct ConvWorker {
     bool live = false;
     int64_t line = 0;
     if (d.halo) {
-      unpack<V>(buf[0], h0);
-      unpack<V>(buf[1], h1);
-      unpack<V>(buf[2], h2);
+      unpack<kF, V>(buf[0], h0);
+      unpack<kF, V>(buf[1], h1);
+      unpack<kF, V>(buf[2], h2);
     } else {
       line = P.cache_indices[(int64_t)d.s * P.ci_stride];
       live = !(P.has_null_block && line == P.null_block_id) && line >= 0 &&
@@ -354,7 +373,7 @@ struct ConvWorker {
     }
 
     auto fix_store = [&](uint32_t word, uint32_t offset) __attribute__((always_inline)) {
-      __builtin_amdgcn_raw_buffer_store_b16((uint16_t)word, orsrc, offset, 0, kStream);
+      store_word(word, offset);
     };
 
     // Rows r0 .. r0 + kGroup - 1 of the tile, of which the first `rows` exist:
@@ -365,7 +384,7 @@ struct ConvWorker {
 #pragma unroll
       for (int g = 0; g < kGroup; ++g) {
         float xv[V];
-        unpack<V>(buf[3 + r0 + g], xv);
+        unpack<kF, V>(buf[3 + r0 + g], xv);
 #pragma unroll
         for (int k = 0; k < V; ++k) {
           float a = bs[k];
@@ -384,40 +403,42 @@ struct ConvWorker {
           }
         }
       }
-      uint32_t words[kGroup][V / 2];
+      constexpr int kWords = row_words<kF, V>();
+      uint32_t words[kGroup][kWords];
       float y[kGroup][V];
-      const bool check = activate_rows<kSilu, V, kGroup>(acc, y, words);
+      uint32_t aux[kGroup][V];
+      const bool check = activate_rows<kF, kSilu, V, kGroup>(acc, y, aux, words);
 #pragma unroll
       for (int g = 0; g < kGroup; ++g) {
         if (g < rows) {
           vec o;
 #pragma unroll
-          for (int i = 0; i < V / 2; ++i) o[i] = words[g][i];
+          for (int i = 0; i < kWords; ++i) o[i] = words[g][i];
           L::template store<kStream>(o, orsrc, ovo, (uint32_t)(d.t0 + r0 + g) * orow_bytes);
         }
       }
       // Rare (any lane): record the elements whose fast word may be wrong; they
       // are rewritten when the list is flushed.
       if (__builtin_expect(__builtin_amdgcn_ballot_w64(check) != 0, 0)) {
-        if (!fix.fits(kGroup * V * kWave)) fix.template flush<kSilu>(lane, fix_store);
+        if (!fix.fits(kGroup * V * kWave)) fix.template flush<kF, kSilu>(lane, fix_store);
 #pragma unroll
         for (int g = 0; g < kGroup; ++g) {
           if (g < rows) {
 #pragma unroll
             for (int k = 0; k < V; ++k)
-              fix.append(needs_exact<kSilu>(acc[g][k], y[g][k]), acc[g][k],
-                         ovo + 2u * k + (uint32_t)(d.t0 + r0 + g) * orow_bytes);
+              fix.append(needs_exact<kF, kSilu>(acc[g][k], y[g][k], aux[g][k]), acc[g][k],
+                         ovo + (uint32_t)(kBytes * k) + (uint32_t)(d.t0 + r0 + g) * orow_bytes);
           }
         }
       }
     };
-    if (d.n == kRows) {
+    if (d.n == R) {
       // Full tile: straight-line code, no conditions.
 #pragma unroll
-      for (int r0 = 0; r0 < kRows; r0 += kGroup) group(r0, kGroup);
+      for (int r0 = 0; r0 < R; r0 += kGroup) group(r0, kGroup);
     } else {
 #pragma unroll
-      for (int r0 = 0; r0 < kRows; r0 += kGroup)
+      for (int r0 = 0; r0 < R; r0 += kGroup)
         if (r0 < d.n) group(r0, min(kGroup, d.n - r0));
     }
 
@@ -426,10 +447,10 @@ struct ConvWorker {
     if (d.j == 0 && live && active) {
       if (d.t0 + d.n < d.end) {
         // The sequence continues past this tile: its last rows are end-3 .. end-1.
-        const __amdgpu_buffer_rsrc_t tr = make_rsrc(P.x + (int64_t)(d.end - 3) * P.x_row_stride);
-        unpack<V>(L::template load<kKeep>(tr, xvo, 0), h0);
-        unpack<V>(L::template load<kKeep>(tr, xvo, xrow_bytes), h1);
-        unpack<V>(L::template load<kKeep>(tr, xvo, 2 * xrow_bytes), h2);
+        const __amdgpu_buffer_rsrc_t tr = make_rsrc(P.x + (int64_t)(d.end - 3) * P.x_row_stride * kBytes);
+        unpack<kF, V>(L::template load<kKeep>(tr, xvo, 0), h0);
+        unpack<kF, V>(L::template load<kKeep>(tr, xvo, xrow_bytes), h1);
+        unpack<kF, V>(L::template load<kKeep>(tr, xvo, 2 * xrow_bytes), h2);
       }
       float* sp = P.states + line * P.cs_stride0;
       if (P.state_vec) {
@@ -456,19 +477,27 @@ struct ConvWorker {
     }
   }
 
+  // One exact word at a byte offset of the launch's output.
+  __device__ __forceinline__ void store_word(uint32_t word, uint32_t offset) {
+    if (kBytes == 4)
+      __builtin_amdgcn_raw_buffer_store_b32(word, orsrc, offset, 0, kStream);
+    else
+      __builtin_amdgcn_raw_buffer_store_b16((uint16_t)word, orsrc, offset, 0, kStream);
+  }
+
   // Rewrites the recorded elements with their exact words.
   __device__ __forceinline__ void finish() {
     auto fix_store = [&](uint32_t word, uint32_t offset) __attribute__((always_inline)) {
-      __builtin_amdgcn_raw_buffer_store_b16((uint16_t)word, orsrc, offset, 0, kStream);
+      store_word(word, offset);
     };
-    fix.template flush<kSilu>(lane, fix_store);
+    fix.template flush<kF, kSilu>(lane, fix_store);
   }
 };
 
 // One wave per tile; a workgroup holds kG waves, the same rows in kG adjacent
 // column blocks. The launch is one-dimensional with the column block varying
 // fastest, so workgroups dispatched together cover whole rows.
-template <int V, int kG, bool kBias, bool kSilu>
+template <int kF, int V, int R, int kG, bool kBias, bool kSilu>
 __global__ __launch_bounds__(kWave * kG) __attribute__((amdgpu_waves_per_eu(kMinWaves))) void packed_conv_kernel(const ConvParams P) {
   static_assert(V % 4 == 0, "the vector weight, bias and state paths take 4 channels at a time");
   const int lane = threadIdx.x % kWave;
@@ -479,11 +508,11 @@ __global__ __launch_bounds__(kWave * kG) __attribute__((amdgpu_waves_per_eu(kMin
   if (cb >= P.col_blocks) return;
   // Weights first: their loads overlap the search for the tile's sequence.
   __shared__ uint2 fix_slots[kG][kFixCapacity];
-  ConvWorker<V, kBias, kSilu> w(P, lane, cb, fix_slots[wave]);
+  ConvWorker<kF, V, R, kBias, kSilu> w(P, lane, cb, fix_slots[wave]);
   w.load_weights();
-  const Tile d = describe_tile(P, p, lane);
+  const Tile d = describe_tile<R>(P, p, lane);
   if (!d.valid) return;
-  typename ConvWorker<V, kBias, kSilu>::Rows buf;
+  typename ConvWorker<kF, V, R, kBias, kSilu>::Rows buf;
   w.issue(buf, d);
   w.compute(buf, d);
   w.finish();
@@ -492,9 +521,9 @@ __global__ __launch_bounds__(kWave * kG) __attribute__((amdgpu_waves_per_eu(kMin
 // The activation map on consecutive FP32 bit patterns, 8 per lane as two rows of 4,
 // through the same activate_rows, needs_exact and FixupList code the convolution
 // uses (one wave per block, so each block owns its list).
-template <bool kSilu>
+template <int kF, bool kSilu>
 __global__ __launch_bounds__(kWave) void activation_map_kernel(uint32_t first, uint64_t count,
-                                                               uint16_t* __restrict__ out) {
+                                                               void* __restrict__ out) {
   const int lane = threadIdx.x;
   const uint64_t block_first = (uint64_t)blockIdx.x * kWave * 8;
   const uint64_t i = block_first + (uint64_t)lane * 8;
@@ -505,46 +534,66 @@ __global__ __launch_bounds__(kWave) void activation_map_kernel(uint32_t first, u
 #pragma unroll
     for (int k = 0; k < 4; ++k) acc[r][k] = __uint_as_float(first + (uint32_t)(i + 4 * r + k));
   }
-  uint32_t w[2][2];
-  const bool check = activate_rows<kSilu, 4, 2>(acc, y, w);
-  *reinterpret_cast<uint4*>(out + i) = make_uint4(w[0][0], w[0][1], w[1][0], w[1][1]);
+  uint32_t w[2][row_words<kF, 4>()];
+  uint32_t aux[2][4];
+  const bool check = activate_rows<kF, kSilu, 4, 2>(acc, y, aux, w);
+  if (kF == kF32) {
+    uint4* o = reinterpret_cast<uint4*>(static_cast<uint32_t*>(out) + i);
+    o[0] = make_uint4(w[0][0], w[0][1], w[0][2], w[0][3]);
+    o[1] = make_uint4(w[1][0], w[1][1], w[1][2], w[1][3]);
+  } else {
+    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + i) = make_uint4(w[0][0], w[0][1], w[1][0], w[1][1]);
+  }
   __shared__ uint2 fix_slots[kFixCapacity];
   FixupList<kFixCapacity> fix{fix_slots, 0u};
-  uint16_t* const block_out = out + block_first;
-  auto fix_store = [&](uint32_t word, uint32_t offset) __attribute__((always_inline)) { block_out[offset] = (uint16_t)word; };
+  auto fix_store = [&](uint32_t word, uint32_t offset) __attribute__((always_inline)) {
+    if (kF == kF32)
+      static_cast<uint32_t*>(out)[block_first + offset] = word;
+    else
+      static_cast<uint16_t*>(out)[block_first + offset] = (uint16_t)word;
+  };
   if (__builtin_amdgcn_ballot_w64(check) != 0) {
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
 #pragma unroll
       for (int k = 0; k < 4; ++k)
-        fix.append(needs_exact<kSilu>(acc[r][k], y[r][k]), acc[r][k], (uint32_t)lane * 8 + 4 * r + k);
+        fix.append(needs_exact<kF, kSilu>(acc[r][k], y[r][k], aux[r][k]), acc[r][k],
+                   (uint32_t)lane * 8 + 4 * r + k);
     }
   }
-  fix.template flush<kSilu>(lane, fix_store);
+  fix.template flush<kF, kSilu>(lane, fix_store);
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-int validate(const void* x, int64_t num_tokens, int64_t dim, int64_t x_row_stride,
+bool known_dtype(int dtype) { return dtype == kBF16 || dtype == kF16 || dtype == kF32; }
+
+int64_t dtype_bytes(int dtype) { return dtype == kF32 ? 4 : 2; }
+
+int validate(const void* x, int dtype, int64_t num_tokens, int64_t dim, int64_t x_row_stride,
              const float* weight, int64_t ws0, int64_t ws1, const float* conv_states,
              int64_t num_cache_lines, int64_t cs0, int64_t cs1, int64_t cs2, const int32_t* qsl,
              int64_t num_seqs, const int32_t* ci, int64_t ci_stride, int64_t part_dim,
              int activation, const void* out) {
   if (num_tokens < 0 || dim < 0 || num_seqs < 0 || num_cache_lines < 0) return KDACONV_EINVAL;
+  if (!known_dtype(dtype)) return KDACONV_EINVAL;
   if (part_dim <= 0 || dim % part_dim != 0) return KDACONV_EINVAL;
   if (x_row_stride < dim) return KDACONV_EINVAL;
   if (activation != KDACONV_ACT_NONE && activation != KDACONV_ACT_SILU) return KDACONV_EINVAL;
-  if (part_dim % 8 != 0 || x_row_stride % 8 != 0) return KDACONV_EUNSUPPORTED;
+  const int64_t eb = dtype_bytes(dtype);
+  // Rows and plane columns start on 16-byte boundaries.
+  if (part_dim % 8 != 0 || (x_row_stride * eb) % 16 != 0) return KDACONV_EUNSUPPORTED;
   if (ws0 < 0 || ws1 < 0 || cs0 < 0 || cs1 < 0 || cs2 < 0 || ci_stride < 0)
     return KDACONV_EUNSUPPORTED;
   // int32 token and sequence indices; 32-bit offsets within a program's rows
   // and within one output plane.
   if (num_tokens > INT32_MAX - 1 || num_seqs > INT32_MAX / 2 || dim > INT32_MAX / 2)
     return KDACONV_EUNSUPPORTED;
-  if (((num_tokens + kRows - 1) / kRows + num_seqs) * ((dim + kWave * kLaneChannels - 1) / (kWave * kLaneChannels)) > INT32_MAX)
+  const int64_t rows = rows_per_tile(dtype);
+  if (((num_tokens + rows - 1) / rows + num_seqs) * ((dim + kWave * kLaneChannels - 1) / (kWave * kLaneChannels)) > INT32_MAX)
     return KDACONV_EUNSUPPORTED;
-  if (x_row_stride * 2 * (kRows + 3) > INT32_MAX) return KDACONV_EUNSUPPORTED;
-  if (num_tokens * part_dim * 2 > INT32_MAX / 2) return KDACONV_EUNSUPPORTED;
+  if (x_row_stride * eb * (rows + 3) > INT32_MAX) return KDACONV_EUNSUPPORTED;
+  if (num_tokens * part_dim * eb > INT32_MAX / 2) return KDACONV_EUNSUPPORTED;
   if (dim * cs1 * 4 > INT32_MAX) return KDACONV_EUNSUPPORTED;
   if (num_tokens == 0 || num_seqs == 0 || dim == 0) return KDACONV_OK;
   if (!x || !weight || !conv_states || !qsl || !ci || !out) return KDACONV_EINVAL;
@@ -552,35 +601,37 @@ int validate(const void* x, int64_t num_tokens, int64_t dim, int64_t x_row_strid
   return KDACONV_OK;
 }
 
-template <int V, int kG>
+template <int kF, int V, int kG>
 void launch_group(const ConvParams& P, bool bias, bool silu, hipStream_t st) {
+  constexpr int R = rows_per_tile<kF>();
   const uint64_t groups = ((uint64_t)P.col_blocks + kG - 1) / kG;
   const dim3 grid((unsigned)((uint64_t)P.programs * groups));
   const dim3 block(kWave * kG);
   if (bias) {
     if (silu)
-      hipLaunchKernelGGL((packed_conv_kernel<V, kG, true, true>), grid, block, 0, st, P);
+      hipLaunchKernelGGL((packed_conv_kernel<kF, V, R, kG, true, true>), grid, block, 0, st, P);
     else
-      hipLaunchKernelGGL((packed_conv_kernel<V, kG, true, false>), grid, block, 0, st, P);
+      hipLaunchKernelGGL((packed_conv_kernel<kF, V, R, kG, true, false>), grid, block, 0, st, P);
   } else {
     if (silu)
-      hipLaunchKernelGGL((packed_conv_kernel<V, kG, false, true>), grid, block, 0, st, P);
+      hipLaunchKernelGGL((packed_conv_kernel<kF, V, R, kG, false, true>), grid, block, 0, st, P);
     else
-      hipLaunchKernelGGL((packed_conv_kernel<V, kG, false, false>), grid, block, 0, st, P);
+      hipLaunchKernelGGL((packed_conv_kernel<kF, V, R, kG, false, false>), grid, block, 0, st, P);
   }
 }
 
-template <int V>
+template <int kF, int V>
 void launch(ConvParams P, int64_t cols, bool bias, bool silu, hipStream_t st) {
+  constexpr int R = rows_per_tile<kF>();
   P.col_blocks = (int32_t)((cols / V + kWave - 1) / kWave);
-  P.programs = (int32_t)((P.num_tokens + kRows - 1) / kRows + P.num_seqs);
-  // Two waves per workgroup measured 3-4 % faster on the 16384 x 4608 workload;
-  // with an odd number of column blocks the second wave of every last workgroup
-  // would idle, and one wave per workgroup is kept.
+  P.programs = (int32_t)((P.num_tokens + R - 1) / R + P.num_seqs);
+  // Two waves per workgroup measured 3-4 % faster on the 16384 x 4608 bf16
+  // workload; with an odd number of column blocks the second wave of every last
+  // workgroup would idle, and one wave per workgroup is kept.
   if (P.col_blocks % 2 == 0)
-    launch_group<V, 2>(P, bias, silu, st);
+    launch_group<kF, V, 2>(P, bias, silu, st);
   else
-    launch_group<V, 1>(P, bias, silu, st);
+    launch_group<kF, V, 1>(P, bias, silu, st);
 }
 
 }  // namespace
@@ -588,7 +639,10 @@ void launch(ConvParams P, int64_t cols, bool bias, bool silu, hipStream_t st) {
 
 using namespace kdaconv;
 
-extern "C" int kdaconv_validate(const void* x, int64_t num_tokens, int64_t dim,
+static_assert(KDACONV_BF16 == kBF16 && KDACONV_F16 == kF16 && KDACONV_F32 == kF32,
+              "format codes of the interface and the kernels agree");
+
+extern "C" int kdaconv_validate(const void* x, int dtype, int64_t num_tokens, int64_t dim,
                                 int64_t x_row_stride, const float* weight, int64_t weight_stride0,
                                 int64_t weight_stride1, const float* bias,
                                 const float* conv_states, int64_t num_cache_lines,
@@ -601,28 +655,29 @@ extern "C" int kdaconv_validate(const void* x, int64_t num_tokens, int64_t dim,
   (void)has_initial_state;
   (void)has_null_block;
   (void)null_block_id;
-  return validate(x, num_tokens, dim, x_row_stride, weight, weight_stride0, weight_stride1,
+  return validate(x, dtype, num_tokens, dim, x_row_stride, weight, weight_stride0, weight_stride1,
                   conv_states, num_cache_lines, cs_stride0, cs_stride1, cs_stride2,
                   query_start_loc, num_seqs, cache_indices, cache_indices_stride, part_dim,
                   activation, out);
 }
 
 extern "C" int kdaconv_packed_causal_conv1d(
-    const void* x, int64_t num_tokens, int64_t dim, int64_t x_row_stride, const float* weight,
-    int64_t weight_stride0, int64_t weight_stride1, const float* bias, float* conv_states,
-    int64_t num_cache_lines, int64_t cs_stride0, int64_t cs_stride1, int64_t cs_stride2,
-    const int32_t* query_start_loc, int64_t num_seqs, const int32_t* cache_indices,
-    int64_t cache_indices_stride, const uint8_t* has_initial_state, int64_t part_dim,
-    int activation, int has_null_block, int64_t null_block_id, void* out,
+    const void* x, int dtype, int64_t num_tokens, int64_t dim, int64_t x_row_stride,
+    const float* weight, int64_t weight_stride0, int64_t weight_stride1, const float* bias,
+    float* conv_states, int64_t num_cache_lines, int64_t cs_stride0, int64_t cs_stride1,
+    int64_t cs_stride2, const int32_t* query_start_loc, int64_t num_seqs,
+    const int32_t* cache_indices, int64_t cache_indices_stride, const uint8_t* has_initial_state,
+    int64_t part_dim, int activation, int has_null_block, int64_t null_block_id, void* out,
     kdaconv_stream_t stream) {
-  const int rc = validate(x, num_tokens, dim, x_row_stride, weight, weight_stride0,
+  const int rc = validate(x, dtype, num_tokens, dim, x_row_stride, weight, weight_stride0,
                           weight_stride1, conv_states, num_cache_lines, cs_stride0, cs_stride1,
                           cs_stride2, query_start_loc, num_seqs, cache_indices,
                           cache_indices_stride, part_dim, activation, out);
   if (rc != KDACONV_OK || num_tokens == 0 || num_seqs == 0 || dim == 0) return rc;
 
+  const int64_t eb = dtype_bytes(dtype);
   ConvParams P;
-  P.x = static_cast<const uint16_t*>(x);
+  P.x = static_cast<const char*>(x);
   P.weight = weight;
   P.bias = bias;
   P.states = conv_states;
@@ -656,9 +711,9 @@ extern "C" int kdaconv_packed_causal_conv1d(
   P.state_vec = cs_stride1 == 3 && cs_stride2 == 1 && cs_stride0 % 4 == 0 && aligned16(conv_states);
 
   // Launches cover groups of whole planes small enough that a lane's offset
-  // into the group's output (planes * num_tokens * part_dim * 2 bytes) stays
-  // below 2^31. One launch in every realistic case.
-  const int64_t plane_bytes = num_tokens * part_dim * 2;
+  // into the group's output (planes * num_tokens * part_dim * element bytes)
+  // stays below 2^31. One launch in every realistic case.
+  const int64_t plane_bytes = num_tokens * part_dim * eb;
   const int64_t planes = dim / part_dim;
   const int64_t per_launch = plane_bytes > 0 ? std::max<int64_t>(1, INT32_MAX / plane_bytes) : planes;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
@@ -667,28 +722,40 @@ extern "C" int kdaconv_packed_causal_conv1d(
     const int64_t pe = std::min(planes, pl + per_launch);
     P.col_begin = (int32_t)(pl * part_dim);
     P.col_end = (int32_t)(pe * part_dim);
-    P.out = static_cast<uint16_t*>(out) + pl * P.plane_stride;
-    launch<kLaneChannels>(P, (pe - pl) * part_dim, bias != nullptr, silu, st);
+    P.out = static_cast<char*>(out) + pl * P.plane_stride * eb;
+    const int64_t cols = (pe - pl) * part_dim;
+    if (dtype == kF32)
+      launch<kF32, kLaneChannels>(P, cols, bias != nullptr, silu, st);
+    else if (dtype == kF16)
+      launch<kF16, kLaneChannels>(P, cols, bias != nullptr, silu, st);
+    else
+      launch<kBF16, kLaneChannels>(P, cols, bias != nullptr, silu, st);
   }
   return hipGetLastError() == hipSuccess ? KDACONV_OK : KDACONV_ELAUNCH;
 }
 
-extern "C" int kdaconv_activation_map(uint32_t first, int64_t count, int activation,
-                                      uint16_t* out, kdaconv_stream_t stream) {
+extern "C" int kdaconv_activation_map(uint32_t first, int64_t count, int activation, int dtype,
+                                      void* out, kdaconv_stream_t stream) {
   if (count < 0 || count % 8 != 0 || count > ((int64_t)1 << 32)) return KDACONV_EINVAL;
   if (activation != KDACONV_ACT_NONE && activation != KDACONV_ACT_SILU) return KDACONV_EINVAL;
+  if (!known_dtype(dtype)) return KDACONV_EINVAL;
   if (count == 0) return KDACONV_OK;
   if (!out) return KDACONV_EINVAL;
   if (!aligned16(out)) return KDACONV_EUNSUPPORTED;
   const uint64_t threads = (uint64_t)count / 8;
   const dim3 grid((unsigned)((threads + kWave - 1) / kWave));
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  if (activation == KDACONV_ACT_SILU)
-    hipLaunchKernelGGL((activation_map_kernel<true>), grid, dim3(kWave), 0, st, first,
-                       (uint64_t)count, out);
-  else
-    hipLaunchKernelGGL((activation_map_kernel<false>), grid, dim3(kWave), 0, st, first,
-                       (uint64_t)count, out);
+  const bool silu = activation == KDACONV_ACT_SILU;
+#define KDACONV_MAP(F, S) \
+  hipLaunchKernelGGL((activation_map_kernel<F, S>), grid, dim3(kWave), 0, st, first, (uint64_t)count, out)
+  if (dtype == kF32) {
+    if (silu) KDACONV_MAP(kF32, true); else KDACONV_MAP(kF32, false);
+  } else if (dtype == kF16) {
+    if (silu) KDACONV_MAP(kF16, true); else KDACONV_MAP(kF16, false);
+  } else {
+    if (silu) KDACONV_MAP(kBF16, true); else KDACONV_MAP(kBF16, false);
+  }
+#undef KDACONV_MAP
   return hipGetLastError() == hipSuccess ? KDACONV_OK : KDACONV_ELAUNCH;
 }
 
@@ -707,4 +774,4 @@ extern "C" const char* kdaconv_status_string(int status) {
   }
 }
 
-extern "C" int kdaconv_version(void) { return 100; }
+extern "C" int kdaconv_version(void) { return 200; }

@@ -1,19 +1,26 @@
 // Device helpers for the packed causal conv kernels (gfx950, wave64).
 //
-// The stored word of an output is bf16(act(acc)) where acc is the FP32
+// The stored word of an output is word(act(acc)) where acc is the FP32
 // accumulator, act is SiLU or the identity, SiLU(a) = a / (1 + exp(-a)) with exp
 // correctly rounded to binary32 and the add and divide rounded to binary32, and
-// bf16() rounds to nearest even (page "vllm.models.kimi_k3.nvidia.ops.kda_conv",
-// module docstring: FP32 arithmetic, SiLU, FP32 -> bf16 round to nearest even).
+// word() is the output format's rounding: bf16 or fp16 to nearest even, or the
+// FP32 value itself; NaN results are stored as the format's canonical quiet NaN
+// (page "vllm.models.kimi_k3.nvidia.ops.kda_conv", module docstring: FP32
+// arithmetic, SiLU, rounding to nearest even; packed_causal_conv1d_fn: output in
+// x's dtype; packed_causal_conv1d_supported: bf16, fp16 or FP32 x).
 //
-// Only the final bf16 word is observable, so SiLU takes a fast path built on the
-// hardware exp2 and reciprocal (a few FP32 ulps off the binary32 SiLU) and the
-// word it rounds to is kept whenever the fast value is farther than that error
-// bound from a bf16 rounding boundary: then the binary32 SiLU lies on the same
-// side and rounds to the same word. The rare rest (and NaN, and large negative
-// accumulators, where the rounded exp2 argument loses accuracy) goes through an
-// exact evaluation in double precision. The map from every FP32 input to its word
-// is checked against the CPU reference on all 2^32 inputs.
+// For the 16-bit formats only the rounded word is observable, so SiLU takes a fast
+// path built on the hardware exp2 and reciprocal (a few FP32 ulps off the binary32
+// SiLU) and the word it rounds to is kept whenever the fast value is farther than
+// that error bound from a rounding boundary of the format: then the binary32 SiLU
+// lies on the same side and rounds to the same word. The rare rest (and NaN, large
+// negative accumulators, where the rounded exp2 argument loses accuracy, and for
+// fp16 the accumulators whose SiLU is an fp16 subnormal) goes through an exact
+// evaluation. The FP32 format stores the binary32 SiLU itself, so every element
+// takes the exact evaluation's main step (exp in double precision, rounded once),
+// and only arguments whose double exp lies near a binary32 rounding boundary go on
+// to a double-double exp. The map from every FP32 input to its word is checked
+// against the CPU reference on all 2^32 inputs, for every format.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -21,12 +28,71 @@
 
 namespace kdaconv {
 
+// Element formats of x and out (the output takes x's format); the numbers are the
+// kdaconv_dtype codes of the C interface.
+enum : int { kBF16 = 0, kF16 = 1, kF32 = 2 };
+
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// Bytes of one element of a format.
+template <int kF>
+constexpr int element_bytes() {
+  return kF == kF32 ? 4 : 2;
+}
+
+// --------------------------------------------------------------------------------------
+// Widening and packing.
+
+// bf16 -> FP32 is exact: the bf16 pattern is the upper half of the FP32 word.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp16 -> FP32 with the hardware conversion (exact for numbers; a signalling NaN
+// comes out quiet with its payload).
+__device__ __forceinline__ float f16_lo(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
+}
+__device__ __forceinline__ float f16_hi(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+
+// Element 0 or 1 of a 32-bit word of a 16-bit format, widened.
+template <int kF>
+__device__ __forceinline__ float widen_half(uint32_t w, int hi) {
+  if (kF == kF16) return hi ? f16_hi(w) : f16_lo(w);
+  return hi ? bf16_hi(w) : bf16_lo(w);
+}
+
+// Two FP32 values -> two words of a 16-bit format, round to nearest even (one
+// v_cvt_pk_bf16_f32 or v_cvt_pk_f16_f32).
+template <int kF>
+__device__ __forceinline__ uint32_t pack_pair(float lo, float hi) {
+  const f32x2 v = {lo, hi};
+  if (kF == kF16) return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// The stored word of a binary32 result, by the format's rule (canonical NaN).
+template <int kF>
+__device__ __forceinline__ uint32_t word_exact(float y) {
+  if (kF == kF32) return y != y ? 0x7FC00000u : __float_as_uint(y);
+  if (kF == kF16) {
+    if (y != y) return 0x7E00u;
+    return __builtin_bit_cast(uint16_t, (_Float16)y);
+  }
+  if (y != y) return 0x7FC0u;
+  const uint32_t u = __float_as_uint(y);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// --------------------------------------------------------------------------------------
+// Fast SiLU for the 16-bit formats.
 
 // Bound, in FP32 ulps (distance between bit patterns), on |fast SiLU - binary32 SiLU|
-// wherever the fast path is trusted. Fast values within this many ulps of a bf16
-// rounding boundary are recomputed exactly.
+// wherever the fast path is trusted. Fast values within this many ulps of a rounding
+// boundary of the output format are recomputed exactly.
 constexpr uint32_t kSiluUlpBound = 16;
 // The fast path is trusted while its exp2 result stays below 2048, which holds for
 // every a above about -7.6 (the product a * -log2(e) is rounded before the exp2, an
@@ -35,16 +101,6 @@ constexpr uint32_t kSiluUlpBound = 16;
 // and every NaN pattern lies above the threshold.
 constexpr uint32_t kFastExpLimitBits = 0x45000000u;  // 2048.0f
 
-// bf16 -> FP32 is exact: the bf16 pattern is the upper half of the FP32 word.
-__device__ __forceinline__ float widen_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float widen_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
-
-// Two FP32 values -> two bf16 words (round to nearest even), one v_cvt_pk_bf16_f32.
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  const f32x2 v = {lo, hi};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-}
-
 // SiLU from the hardware exp2 and reciprocal; e receives the exp2 result, which
 // decides whether the value can be trusted (kFastExpLimitBits).
 __device__ __forceinline__ float silu_fast(float a, float& e) {
@@ -52,90 +108,214 @@ __device__ __forceinline__ float silu_fast(float a, float& e) {
   return a * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
-// Key of a fast value: its low half-word moved to the top plus an offset, so that
-// the key is at least kNearKey exactly when the half-word lies within
-// kSiluUlpBound of 0x8000, the point halfway between two bf16 numbers.
-constexpr uint32_t kNearKey = (0x10000u - 2u * kSiluUlpBound - 1u) << 16;
-constexpr uint32_t kNearOffset = 0u - ((0x8000u + kSiluUlpBound + 1u) << 16);
+// Nearness keys. A format keeps the upper bits of the FP32 word and drops the low
+// kDrop bits (16 for bf16, 13 for fp16 in its normal range); the value is halfway
+// between two neighbours of the format when the dropped bits equal 2^(kDrop-1). The
+// key moves the dropped bits to the top of a word and adds an offset, so that it is
+// at least near_limit<kDrop>() exactly when the dropped bits lie within kSiluUlpBound
+// of the halfway point.
+template <int kDrop>
+constexpr uint32_t near_limit() {
+  return ((1u << kDrop) - 2u * kSiluUlpBound - 1u) << (32 - kDrop);
+}
+template <int kDrop>
+constexpr uint32_t near_offset() {
+  return 0u - (((1u << (kDrop - 1)) + kSiluUlpBound + 1u) << (32 - kDrop));
+}
+template <int kDrop>
 __device__ __forceinline__ uint32_t near_key(float y) {
-  return (__float_as_uint(y) << 16) + kNearOffset;
+  return (__float_as_uint(y) << (32 - kDrop)) + near_offset<kDrop>();
 }
 // The same key in one instruction (the compiler emits a shift and an add, since the
-// fused form takes no literal operand): offset must hold kNearOffset.
+// fused form takes no literal operand): offset must hold near_offset<kDrop>().
+template <int kDrop>
 __device__ __forceinline__ uint32_t near_key_fused(float y, uint32_t offset) {
   uint32_t key;
-  asm("v_lshl_add_u32 %0, %1, 16, %2" : "=v"(key) : "v"(y), "s"(offset));
+  asm("v_lshl_add_u32 %0, %1, %2, %3" : "=v"(key) : "v"(y), "n"(32 - kDrop), "s"(offset));
   return key;
 }
 
-// FP32 -> bf16 word, round to nearest even, NaN -> 0x7FC0.
-__device__ __forceinline__ uint32_t bf16_word_exact(float y) {
-  if (y != y) return 0x7FC0u;
-  const uint32_t u = __float_as_uint(y);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
-// The exact path is out of line (a call), so its double-precision temporaries do
-// not count against the register budget of the streaming loop that rarely needs
-// it (0 = inline).
-#ifndef KDACONV_EXACT_OUTLINED
-#define KDACONV_EXACT_OUTLINED 1
-#endif
-#if KDACONV_EXACT_OUTLINED
-#define KDACONV_EXACT_INLINE __noinline__
-#else
-#define KDACONV_EXACT_INLINE __forceinline__
-#endif
-
-// The stored word by the defining steps. exp runs in double precision and is
-// rounded once to binary32; the quotient is formed in double from the two binary32
-// operands and rounded once to binary32, which equals the binary32 quotient (53 >=
-// 2 * 24 + 2 bits, so the double rounding is innocuous).
-__device__ KDACONV_EXACT_INLINE uint32_t act_word_exact(float a, bool silu) {
-  float y = a;
-  if (silu) {
-    const float e = (float)exp(-(double)a);
-    const float d = 1.0f + e;
-    y = (float)((double)a / (double)d);
-  }
-  return bf16_word_exact(y);
+// Dropped bits of each 16-bit format (fp16: normal range; subnormal results are
+// sent to the exact path separately).
+template <int kF>
+constexpr int dropped_bits() {
+  return kF == kF16 ? 13 : 16;
 }
 
 // Accumulators at or below this bound take the exact path. Every a with exp2 result
 // at least 2048 (kFastExpLimitBits) lies below about -7.62, so the per-element test
-// below flags a superset of what the reduction in activate_rows detects.
+// flags a superset of what the reduction in activate_rows detects.
 constexpr float kExactBelow = -7.5f;
+// fp16: a SiLU below 2^-14 in magnitude is an fp16 subnormal, whose rounding
+// boundaries the key does not see. For a above kExactBelow that needs |a| < 2^-12.6
+// (SiLU(a) = a * sigmoid(a) with sigmoid(a) > 0.4 there), so |a| < 2^-12 goes exact.
+constexpr float kTinyF16 = 0x1p-12f;
 
-// Does the fast word of accumulator a (fast value y) need the exact path? SiLU:
-// y near a bf16 rounding boundary, or a below kExactBelow, or NaN; identity: NaN.
-template <bool kSilu>
-__device__ __forceinline__ bool needs_exact(float a, float y) {
-  if (kSilu) return near_key(y) >= kNearKey || !(a >= kExactBelow);
-  return a != a;
+// --------------------------------------------------------------------------------------
+// Exact evaluation.
+
+// exp in double precision, rounded once to binary32, and the key of the dropped bits
+// of the double value: the binary32 rounding keeps the top 23 of its 52 fraction bits,
+// so the low 29 bits of the low word decide it, halfway at 2^28. The key is at least
+// kDoubleNearLimit when they lie within 2^12 of halfway (about 2^-40 relative), far
+// wider than the error of the double exp; only those arguments need more precision.
+// The key does not apply where the binary32 result is subnormal (a > 87.3), where
+// 1 + exp(-a) rounds to 1 whatever the last bit of exp(-a), nor does any result there
+// need it.
+constexpr uint32_t kDoubleWindow = 1u << 12;
+constexpr uint32_t kDoubleNearLimit = ((1u << 29) - 2u * kDoubleWindow - 1u) << 3;
+constexpr uint32_t kDoubleNearOffset = 0u - (((1u << 28) + kDoubleWindow + 1u) << 3);
+
+__device__ __forceinline__ float exp_neg_double(float a, uint32_t& key) {
+  const double ed = exp(-(double)a);
+  key = ((uint32_t)__double_as_longlong(ed) << 3) + kDoubleNearOffset;
+  return (float)ed;
 }
 
-// R rows of N accumulators -> R rows of N fast words, two per 32-bit word (element k
-// of a row in half-word k & 1 of word k / 2); y receives the fast values. Returns
-// whether any element may need the exact path. The test is a reduction over all
-// R * N elements (unsigned maxima of the keys and of the exp2 bit patterns; for the
-// identity, a sum that is NaN if any term is) followed by one compare, so it costs
-// about one instruction per element; a true result is followed by needs_exact on
-// each element.
-template <bool kSilu, int N, int R>
+// Double-double helpers (Knuth's two-sum and the FMA two-product).
+__device__ __forceinline__ void two_sum(double a, double b, double& s, double& e) {
+  s = a + b;
+  const double bb = s - a;
+  e = (a - (s - bb)) + (b - bb);
+}
+__device__ __forceinline__ void quick_two_sum(double a, double b, double& s, double& e) {
+  s = a + b;
+  e = b - (s - a);
+}
+
+// exp(x) as hi + lo with a relative error far below 2^-90, for binary32 x with
+// |x| <= 104 (beyond, the binary32 result is 0, a subnormal that cannot matter, or
+// infinity). Argument reduction x = k ln2 + r with ln 2 as a double-double, then
+// exp(r) = 1 + r/1 (1 + r/2 (1 + ... (1 + r/22))) in double-double arithmetic
+// (|r| <= 0.35, so the dropped terms are below 2^-103), scaled by 2^k.
+__device__ __forceinline__ void exp_double_double(float x, double& hi, double& lo) {
+  const double kLn2Hi = 0x1.62e42fefa39efp-1;
+  const double kLn2Lo = 0x1.abc9e3b39803fp-56;
+  const double xd = (double)x;
+  const double k = __builtin_rint(xd * 0x1.71547652b82fep+0);
+  // k * kLn2Hi exactly as ph + pl; x - ph is exact (Sterbenz: x and ph within a
+  // factor of two whenever k != 0).
+  const double ph = k * kLn2Hi;
+  const double pl = __builtin_fma(k, kLn2Hi, -ph);
+  double rh, rl;
+  two_sum(xd - ph, -pl, rh, rl);
+  rl -= k * kLn2Lo;
+  quick_two_sum(rh, rl, rh, rl);
+  double sh = 1.0, sl = 0.0;
+#pragma unroll 1
+  for (int n = 22; n >= 1; --n) {
+    // (sh, sl) * (rh, rl)
+    double th = sh * rh;
+    double tl = __builtin_fma(sh, rh, -th) + (sh * rl + sl * rh);
+    quick_two_sum(th, tl, th, tl);
+    // / n: q = th / n, remainder th - q n exact by FMA
+    const double dn = (double)n;
+    const double qh = th / dn;
+    const double rem = __builtin_fma(-qh, dn, th);
+    const double ql = (rem + tl) / dn;
+    // 1 + q
+    double uh, ul;
+    two_sum(1.0, qh, uh, ul);
+    ul += ql;
+    quick_two_sum(uh, ul, sh, sl);
+  }
+  const int ki = (int)k;
+  hi = __builtin_ldexp(sh, ki);
+  lo = __builtin_ldexp(sl, ki);
+}
+
+// exp(x) correctly rounded to binary32 (normal results; subnormal results may be one
+// unit off at an exact double midpoint, which no use here can observe).
+__device__ __forceinline__ float exp_binary32_escalated(float x) {
+  if (!(x >= -104.0f)) return x != x ? x : 0.0f;
+  if (x > 104.0f) return __builtin_inff();
+  double hi, lo;
+  exp_double_double(x, hi, lo);
+  // hi is the double nearest to hi + lo, so rounding hi to binary32 is right unless
+  // hi is itself halfway between two binary32 numbers; then lo's sign decides.
+  const uint64_t bits = (uint64_t)__double_as_longlong(hi);
+  if ((bits & 0x1FFFFFFFull) == 0x10000000ull && lo != 0.0)
+    hi = lo > 0.0 ? __longlong_as_double((long long)(bits + 1)) : __longlong_as_double((long long)(bits - 1));
+  return (float)hi;
+}
+
+// exp(-a) correctly rounded to binary32 (within the normal range, see above).
+__device__ __forceinline__ float exp_neg_binary32(float a) {
+  uint32_t key;
+  const float e = exp_neg_double(a, key);
+  if (key >= kDoubleNearLimit) return exp_binary32_escalated(-a);
+  return e;
+}
+
+// The binary32 SiLU by the defining steps.
+__device__ __forceinline__ float silu_binary32(float a) {
+  const float e = exp_neg_binary32(a);
+  const float d = 1.0f + e;
+  return a / d;
+}
+
+// The exact path is out of line (a call), so its double-precision temporaries do
+// not count against the register budget of the streaming code that rarely needs it.
+template <int kF>
+__device__ __noinline__ uint32_t act_word_exact(float a, bool silu) {
+  return word_exact<kF>(silu ? silu_binary32(a) : a);
+}
+
+// --------------------------------------------------------------------------------------
+// Activation of rows of accumulators.
+
+// Does the word of accumulator a (value y, aux from activate_rows) need the exact
+// path? SiLU, 16-bit formats: y near a rounding boundary, a below kExactBelow, NaN,
+// or (fp16) a subnormal result; SiLU, FP32: the double exp near a binary32 rounding
+// boundary, or a NaN value; identity: NaN.
+template <int kF, bool kSilu>
+__device__ __forceinline__ bool needs_exact(float a, float y, uint32_t aux) {
+  if (!kSilu) return a != a;
+  if (kF == kF32) return aux >= kDoubleNearLimit || y != y;
+  constexpr int kDrop = dropped_bits<kF>();
+  const bool near = near_key<kDrop>(y) >= near_limit<kDrop>() || !(a >= kExactBelow);
+  if (kF == kF16) return near || __builtin_fabsf(a) < kTinyF16;
+  return near;
+}
+
+// Words per row of N elements.
+template <int kF, int N>
+constexpr int row_words() {
+  return kF == kF32 ? N : N / 2;
+}
+
+// R rows of N accumulators -> R rows of words (16-bit formats: element k of a row in
+// half-word k & 1 of word k / 2; FP32: one word per element); y receives the values
+// whose words were formed, aux what needs_exact takes besides. Returns whether any
+// element may need the exact path. The test is a reduction over all R * N elements
+// (unsigned maxima of keys and of exp2 bit patterns, a minimum of magnitudes, or a
+// sum that is NaN if any term is) followed by one compare, so it costs about one
+// instruction per element; a true result is followed by needs_exact on each element.
+template <int kF, bool kSilu, int N, int R>
 __device__ __forceinline__ bool activate_rows(const float (&acc)[R][N], float (&y)[R][N],
-                                              uint32_t (&w)[R][N / 2]) {
-  const uint32_t offset = kNearOffset;
+                                              uint32_t (&aux)[R][N],
+                                              uint32_t (&w)[R][row_words<kF, N>()]) {
+  constexpr int kDrop = dropped_bits<kF>();
+  const uint32_t offset = near_offset<kDrop>();
   uint32_t key_max = 0, exp_max = 0;
   float sum = 0.0f;
+  float amin = __builtin_inff();
 #pragma unroll
   for (int r = 0; r < R; ++r) {
 #pragma unroll
     for (int k = 0; k < N; ++k) {
-      if (kSilu) {
+      aux[r][k] = 0;
+      if (kSilu && kF == kF32) {
+        const float e = exp_neg_double(acc[r][k], aux[r][k]);
+        y[r][k] = acc[r][k] / (1.0f + e);
+        key_max = max(key_max, aux[r][k]);
+        sum += y[r][k];
+      } else if (kSilu) {
         float e;
         y[r][k] = silu_fast(acc[r][k], e);
-        key_max = max(key_max, near_key_fused(y[r][k], offset));
+        key_max = max(key_max, near_key_fused<kDrop>(y[r][k], offset));
         exp_max = max(exp_max, __float_as_uint(e));
+        if (kF == kF16) amin = __builtin_fminf(amin, __builtin_fabsf(acc[r][k]));
       } else {
         y[r][k] = acc[r][k];
         sum += acc[r][k];
@@ -144,18 +324,27 @@ __device__ __forceinline__ bool activate_rows(const float (&acc)[R][N], float (&
   }
 #pragma unroll
   for (int r = 0; r < R; ++r) {
+    if (kF == kF32) {
 #pragma unroll
-    for (int i = 0; i < N / 2; ++i) w[r][i] = pack_bf16x2(y[r][2 * i], y[r][2 * i + 1]);
+      for (int k = 0; k < N; ++k) w[r][k] = __float_as_uint(y[r][k]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < N / 2; ++i) w[r][i] = pack_pair<kF>(y[r][2 * i], y[r][2 * i + 1]);
+    }
   }
-  return kSilu ? (key_max >= kNearKey || exp_max >= kFastExpLimitBits) : sum != sum;
+  if (!kSilu) return sum != sum;
+  if (kF == kF32) return key_max >= kDoubleNearLimit || sum != sum;
+  const bool flag = key_max >= near_limit<kDrop>() || exp_max >= kFastExpLimitBits;
+  if (kF == kF16) return flag || amin < kTinyF16;
+  return flag;
 }
 
-// Elements whose fast word must be replaced, collected per wave in LDS and
-// rewritten with their exact words in passes of 64 (one per lane). Deferring
-// them lets a wave run the exact path once for the elements of many rows instead
-// of once per row group in which any of its 64 lanes needs it. A flush first waits
-// for the wave's earlier stores, so each exact word lands after the fast word it
-// replaces. count is uniform across the wave.
+// Elements whose word must be replaced, collected per wave in LDS and rewritten
+// with their exact words in passes of 64 (one per lane). Deferring them lets a
+// wave run the exact path once for the elements of many rows instead of once per
+// row group in which any of its 64 lanes needs it. A flush first waits for the
+// wave's earlier stores, so each exact word lands after the word it replaces.
+// count is uniform across the wave.
 template <int kCapacity>
 struct FixupList {
   uint2* slots;  // kCapacity entries {accumulator bits, output offset} in LDS
@@ -178,9 +367,9 @@ struct FixupList {
     return count + incoming <= (uint32_t)kCapacity;
   }
 
-  // Writes the exact word of every entry through store(word, offset) and empties
-  // the list.
-  template <bool kSilu, class Store>
+  // Writes the exact word (format kF) of every entry through store(word, offset)
+  // and empties the list.
+  template <int kF, bool kSilu, class Store>
   __device__ __forceinline__ void flush(int lane, Store store) {
     if (count == 0) return;
     __builtin_amdgcn_s_waitcnt(0);  // earlier stores of this wave have completed
@@ -188,7 +377,7 @@ struct FixupList {
       const uint32_t i = base + (uint32_t)lane;
       if (i < count) {
         const uint2 e = slots[i];
-        store(act_word_exact(__uint_as_float(e.x), kSilu), e.y);
+        store(act_word_exact<kF>(__uint_as_float(e.x), kSilu), e.y);
       }
     }
     count = 0;

@@ -41,10 +41,11 @@ A = 0x10000
 
 
 def _args(**kw):
-    a = dict(x=A, T=64, dim=384, sx=384, w=A, ws0=4, ws1=1, b=A, st=A, lines=4, cs0=1152, cs1=3,
-             cs2=1, qsl=A, S=2, ci=A, cis=1, init=A, pd=128, act=1, hn=0, nid=0, out=A)
+    a = dict(x=A, dt=_lib.BF16, T=64, dim=384, sx=384, w=A, ws0=4, ws1=1, b=A, st=A, lines=4,
+             cs0=1152, cs1=3, cs2=1, qsl=A, S=2, ci=A, cis=1, init=A, pd=128, act=1, hn=0, nid=0,
+             out=A)
     a.update(kw)
-    return [a["x"], a["T"], a["dim"], a["sx"], a["w"], a["ws0"], a["ws1"], a["b"], a["st"],
+    return [a["x"], a["dt"], a["T"], a["dim"], a["sx"], a["w"], a["ws0"], a["ws1"], a["b"], a["st"],
             a["lines"], a["cs0"], a["cs1"], a["cs2"], a["qsl"], a["S"], a["ci"], a["cis"],
             a["init"], a["pd"], a["act"], a["hn"], a["nid"], a["out"]]
 
@@ -74,6 +75,15 @@ def _args(**kw):
     (dict(T=0, x=0, out=0), _lib.OK),  # nothing to do: no launch, pointers unused
     (dict(S=0, qsl=0), _lib.OK),
     (dict(T=1 << 31), _lib.EUNSUPPORTED),
+    (dict(dt=3), _lib.EINVAL),  # unknown format
+    (dict(dt=-1), _lib.EINVAL),
+    (dict(dt=_lib.F16), _lib.OK),
+    (dict(dt=_lib.F32), _lib.OK),
+    (dict(dt=_lib.F16, sx=388), _lib.EUNSUPPORTED),  # fp16 rows 776 bytes apart
+    (dict(dt=_lib.F32, sx=388), _lib.OK),  # FP32 rows 1552 bytes apart
+    (dict(dt=_lib.F32, sx=386), _lib.EUNSUPPORTED),
+    (dict(dt=_lib.F32, T=1 << 25, pd=8, dim=8, sx=8), _lib.EUNSUPPORTED),  # plane of 2^30 bytes
+    (dict(dt=_lib.BF16, T=1 << 25, pd=8, dim=8, sx=8), _lib.OK),
 ])
 def test_validate_status_codes(kw, code):
     lib = _lib.load()
@@ -82,11 +92,12 @@ def test_validate_status_codes(kw, code):
 
 def test_activation_map_argument_errors():
     lib = _lib.load()
-    assert lib.kdaconv_activation_map(0, 7, 1, A, None) == _lib.EINVAL  # not a multiple of 8
-    assert lib.kdaconv_activation_map(0, 8, 5, A, None) == _lib.EINVAL
-    assert lib.kdaconv_activation_map(0, 8, 1, None, None) == _lib.EINVAL
-    assert lib.kdaconv_activation_map(0, 8, 1, A + 2, None) == _lib.EUNSUPPORTED
-    assert lib.kdaconv_activation_map(0, 0, 1, None, None) == _lib.OK
+    assert lib.kdaconv_activation_map(0, 7, 1, 0, A, None) == _lib.EINVAL  # not a multiple of 8
+    assert lib.kdaconv_activation_map(0, 8, 5, 0, A, None) == _lib.EINVAL
+    assert lib.kdaconv_activation_map(0, 8, 1, 3, A, None) == _lib.EINVAL  # unknown format
+    assert lib.kdaconv_activation_map(0, 8, 1, 0, None, None) == _lib.EINVAL
+    assert lib.kdaconv_activation_map(0, 8, 1, 2, A + 2, None) == _lib.EUNSUPPORTED
+    assert lib.kdaconv_activation_map(0, 0, 1, 1, None, None) == _lib.OK
 
 
 def test_python_checks_reject_host_tensors_and_bad_args():
@@ -99,6 +110,9 @@ def test_python_checks_reject_host_tensors_and_bad_args():
     with pytest.raises(ValueError):
         kd.packed_causal_conv1d_fn(x, w, None, st, q, ci, init, 8)
     assert not kd.packed_causal_conv1d_supported(x, w, st, 8)
+    with pytest.raises(ValueError):
+        kd._dtype_code(torch.float64)
+    assert kd._dtype_code(torch.float16) == _lib.F16 and kd._dtype_code(torch.float32) == _lib.F32
     with pytest.raises(ValueError):
         kd._activation_code("gelu")
     assert kd._activation_code("swish") == _lib.ACT_SILU

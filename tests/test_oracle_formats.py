@@ -229,3 +229,20 @@ def test_unknown_format_rejected(olib):
         wl.query_start_loc.ctypes.data, 1, wl.cache_indices.ctypes.data, 1, None, 8, 1, 0, 0,
         np.zeros(24, dtype=np.uint16).ctypes.data)
     assert rc == 1
+
+
+def test_workload_formats_share_draws():
+    """The x format changes no draw: the FP32 inputs of a fuzz case round to its bf16
+    and fp16 inputs, and the other arrays are identical."""
+    import workloads
+
+    for seed in (3, 2001):
+        b = workloads.random_case(seed, x_dtype="bf16")
+        h = workloads.random_case(seed, x_dtype="f16")
+        f = workloads.random_case(seed, x_dtype="f32")
+        vals = f.x[:, : f.dim].view(np.float32)
+        assert np.array_equal(workloads.f32_to_bf16_bits(vals), b.x[:, : b.dim])
+        assert np.array_equal(vals.astype(np.float16).view(np.uint16), h.x[:, : h.dim])
+        assert np.all(f.x[:, f.dim:] == workloads.CANARIES["f32"])
+        for name in ("weight", "conv_states", "query_start_loc", "cache_indices"):
+            assert np.array_equal(getattr(b, name), getattr(f, name))

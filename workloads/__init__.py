@@ -256,7 +256,7 @@ CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}
 def random_case(seed: int, *, max_seqs: int = 12, max_len: int = 200, parts: int = 3,
                 part_dim: Optional[int] = None, x_scale: float = 1.0,
                 allow_empty: bool = True, pad_tokens: int = 0,
-                row_pad: Optional[int] = None) -> Workload:
+                row_pad: Optional[int] = None, x_dtype: str = "bf16") -> Workload:
     """Random fuzz case: zero-length sequences, null block, strides, padding rows.
 
     ``x_scale`` widens the accumulator range so that large negative and positive
