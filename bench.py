@@ -67,6 +67,13 @@ def counter_traffic():
         return None
 
 
+def x_tensor(torch, wl, dev):
+    """The workload's whole row-strided x buffer on the device, in its format."""
+    dt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[wl.x_dtype]
+    signed = np.int32 if wl.x.dtype == np.uint32 else np.int16
+    return torch.from_numpy(np.ascontiguousarray(wl.x).view(signed)).to(dev).view(dt)
+
+
 def time_config(kd, torch, wl, steps: int, warmup: int, sets: int = 2):
     """Per-launch HIP-event times of the kernel on one workload, with `sets` complete
     input/output/state sets rotated (two sets of the 16K-token workloads exceed the
@@ -74,14 +81,14 @@ def time_config(kd, torch, wl, steps: int, warmup: int, sets: int = 2):
     use)."""
     dev = torch.device("cuda:0")
     P = wl.dim // wl.part_dim
-    xb = torch.from_numpy(np.ascontiguousarray(wl.x).view(np.int16)).to(dev).view(torch.bfloat16)
+    xb = x_tensor(torch, wl, dev)
     bufs = []
     for i in range(sets):
         x = xb.clone() if i else xb
         bufs.append(dict(
             x=x[:, : wl.dim],
             st=torch.from_numpy(wl.conv_states.copy()).to(dev),
-            out=torch.empty((P, wl.num_tokens, wl.part_dim), dtype=torch.bfloat16, device=dev),
+            out=torch.empty((P, wl.num_tokens, wl.part_dim), dtype=xb.dtype, device=dev),
         ))
     w = torch.from_numpy(wl.weight).to(dev)
     b = None if wl.bias is None else torch.from_numpy(wl.bias).to(dev)
@@ -109,7 +116,7 @@ def time_config(kd, torch, wl, steps: int, warmup: int, sets: int = 2):
     med = float(np.median(us))
     nbytes = wl.algorithmic_bytes()
     return {
-        "workload": wl.name,
+        "workload": wl.name + ("" if wl.x_dtype == "bf16" else f", x and out {wl.x_dtype}"),
         "algorithmic_bytes": nbytes,
         "kernel_us_median": round(med, 3),
         "kernel_us_p10_p90": [round(float(np.percentile(us, 10)), 3),
@@ -268,6 +275,11 @@ def main() -> int:
         result["other_configs"] = {
             str(k): time_config(kd, torch, workloads.CONFIGS[k](), steps=100, warmup=10)
             for k in (1, 2, 4, 5)
+        }
+        # The same 16K-token workload with fp16 and FP32 x (output in x's format).
+        result["other_formats"] = {
+            fmt: time_config(kd, torch, workloads.config3(x_dtype=fmt), steps=100, warmup=10)
+            for fmt in ("f16", "f32")
         }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_runs)

@@ -88,6 +88,11 @@ typedef enum kdaconv_dtype {
  * conv_states        FP32, logical shape (num_cache_lines, dim, 3): history k of
  *                    channel c of line l at conv_states[l * cs_stride0 +
  *                    c * cs_stride1 + k * cs_stride2]. Read and written in place.
+ *                    Any layout the strides describe: (lines, dim, 3) contiguous and
+ *                    "dim first" (lines, 3, dim) take vector paths; a state wider
+ *                    than 3 (lines, dim, W) passes its strides, entries 0..2 are the
+ *                    history and the rest are not touched (the page's launch passes
+ *                    the three strides and not the width).
  * query_start_loc    int32 (num_seqs + 1): sequence s owns rows [qsl[s], qsl[s+1]).
  *                    Must be non-decreasing with qsl[num_seqs] <= num_tokens; rows
  *                    outside every sequence are neither read nor written.

@@ -187,7 +187,8 @@ def packed_causal_conv1d(x: np.ndarray, dim: int, weight: np.ndarray, bias: Opti
     assert x.dtype == wd and x.ndim == 2 and x.strides[1] == esize
     assert weight.dtype == np.float32 and weight.ndim == 2 and weight.shape == (dim, 4)
     assert conv_states.dtype == np.float32 and conv_states.ndim == 3
-    assert conv_states.shape[1] == dim and conv_states.shape[2] == 3
+    # The state is entries 0..2 of the last axis; wider states keep the rest untouched.
+    assert conv_states.shape[1] == dim and conv_states.shape[2] >= 3
     assert query_start_loc.dtype == np.int32 and cache_indices.dtype == np.int32
     if bias is not None:
         assert bias.dtype == np.float32 and bias.shape == (dim,) and bias.flags.c_contiguous

@@ -94,8 +94,8 @@ def _check_tensors(x, weight, bias, conv_states, query_start_loc, cache_indices,
         raise ValueError("bias must be a contiguous float32 (dim,) tensor or None")
     if conv_states.dtype != torch.float32 or conv_states.dim() != 3 or conv_states.size(1) != dim:
         raise ValueError("conv_states must be float32 of shape (cache lines, dim, 3)")
-    if conv_states.size(2) != 3:
-        raise ValueError("conv_states must have exactly 3 history entries per channel")
+    if conv_states.size(2) < 3:
+        raise ValueError("conv_states needs at least 3 history entries per channel")
     if query_start_loc.dtype != torch.int32 or query_start_loc.dim() != 1:
         raise ValueError("query_start_loc must be a 1-D int32 tensor")
     if not query_start_loc.is_contiguous():
@@ -166,7 +166,8 @@ def packed_causal_conv1d_supported(x: torch.Tensor, weight: torch.Tensor,
     """Whether packed_causal_conv1d_fn serves these tensors (page:
     packed_causal_conv1d_supported). This build takes bf16, fp16 or FP32 x with
     unit column stride and rows 16 bytes apart, FP32 weight (dim, 4), FP32
-    conv_states (lines, dim, 3), and part_dim a multiple of 8 dividing dim."""
+    conv_states (lines, dim, >= 3) in any strided layout (entries 0..2 of the last
+    axis are the history), and part_dim a multiple of 8 dividing dim."""
     try:
         if not (x.is_cuda and x.dim() == 2 and x.stride(1) == 1 and x.dtype in _DTYPE_CODES):
             return False
@@ -174,7 +175,7 @@ def packed_causal_conv1d_supported(x: torch.Tensor, weight: torch.Tensor,
                 and tuple(weight.shape) == (x.size(1), 4)):
             return False
         if not (conv_states.dtype == torch.float32 and conv_states.dim() == 3
-                and conv_states.size(1) == x.size(1) and conv_states.size(2) == 3):
+                and conv_states.size(1) == x.size(1) and conv_states.size(2) >= 3):
             return False
         if part_dim <= 0 or x.size(1) % part_dim != 0:
             return False

@@ -131,6 +131,8 @@ struct ConvParams {
   int32_t weight_vec;  // weight is (dim, 4) contiguous and 16-byte aligned
   int32_t bias_vec;  // bias is 16-byte aligned
   int32_t state_vec;  // each state line is (dim, 3) contiguous and 16-byte aligned
+  int32_t state_rows;  // each state line is 3 rows of dim contiguous channels ("dim first"),
+                       // 16-byte aligned, row and line strides multiples of 4
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
@@ -357,6 +359,23 @@ struct ConvWorker {
             h1[k] = f[3 * k + 1];
             h2[k] = f[3 * k + 2];
           }
+        } else if (P.state_rows) {
+          // History k of the lane's V channels: V consecutive floats of row k.
+          const __amdgpu_buffer_rsrc_t sr = make_rsrc(sp);
+          const uint32_t row = (uint32_t)P.cs_stride2 * 4u;
+#pragma unroll
+          for (int i = 0; i < V / 4; ++i) {
+            const uint32_t o = (uint32_t)(cl + 4 * i) * 4u;
+            const u32x4 t0 = __builtin_amdgcn_raw_buffer_load_b128(sr, o, 0, kKeep);
+            const u32x4 t1 = __builtin_amdgcn_raw_buffer_load_b128(sr, o + row, 0, kKeep);
+            const u32x4 t2 = __builtin_amdgcn_raw_buffer_load_b128(sr, o + 2 * row, 0, kKeep);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              h0[4 * i + k] = __uint_as_float(t0[k]);
+              h1[4 * i + k] = __uint_as_float(t1[k]);
+              h2[4 * i + k] = __uint_as_float(t2[k]);
+            }
+          }
         } else {
 #pragma unroll
           for (int k = 0; k < V; ++k) {
@@ -465,6 +484,16 @@ struct ConvWorker {
 #pragma unroll
         for (int i = 0; i < 3 * V / 4; ++i)
           sv[i] = make_float4(f[4 * i], f[4 * i + 1], f[4 * i + 2], f[4 * i + 3]);
+      } else if (P.state_rows) {
+#pragma unroll
+        for (int i = 0; i < V / 4; ++i) {
+          float* cp = sp + cl + 4 * i;
+          *reinterpret_cast<float4*>(cp) = make_float4(h0[4 * i], h0[4 * i + 1], h0[4 * i + 2], h0[4 * i + 3]);
+          *reinterpret_cast<float4*>(cp + P.cs_stride2) =
+              make_float4(h1[4 * i], h1[4 * i + 1], h1[4 * i + 2], h1[4 * i + 3]);
+          *reinterpret_cast<float4*>(cp + 2 * P.cs_stride2) =
+              make_float4(h2[4 * i], h2[4 * i + 1], h2[4 * i + 2], h2[4 * i + 3]);
+        }
       } else {
 #pragma unroll
         for (int k = 0; k < V; ++k) {
@@ -709,6 +738,8 @@ extern "C" int kdaconv_packed_causal_conv1d(
   P.weight_vec = weight_stride0 == 4 && weight_stride1 == 1 && aligned16(weight);
   P.bias_vec = bias != nullptr && aligned16(bias);
   P.state_vec = cs_stride1 == 3 && cs_stride2 == 1 && cs_stride0 % 4 == 0 && aligned16(conv_states);
+  P.state_rows = cs_stride1 == 1 && cs_stride2 >= dim && cs_stride2 % 4 == 0 && cs_stride0 % 4 == 0 &&
+                 aligned16(conv_states) && (2 * cs_stride2 + dim) * 4 < INT32_MAX;
 
   // Launches cover groups of whole planes small enough that a lane's offset
   // into the group's output (planes * num_tokens * part_dim * element bytes)

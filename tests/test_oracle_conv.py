@@ -309,3 +309,37 @@ def test_against_torch_conv1d_float64(olib, seed, silu):
     # four fused roundings of the chain, SiLU's own rounding (slope <= 1.1), one bf16 rounding
     tol = 8 * 2.0 ** -24 * mag + 4 * 2.0 ** -24 * np.abs(ref) + bf16_ulp(ref) * 0.5 + 1e-30
     assert np.all(np.abs(g - ref) <= tol)
+
+
+# ------------------------------------------------------- conv-state layouts
+
+def test_wide_state_uses_entries_zero_to_two(olib):
+    """A state wider than 3 (the page's check admits size(2) >= 3 and its launch
+    passes the three strides, not the size): entries 0..2 are the history and the
+    rest stay as they were."""
+    wl = make_workload([5, 2, 9, 1], dim=16, part_dim=8, seed=48, init=[True, True, False, True])
+    o_ref, st_ref = oracle.run_workload(wl, lib=olib)
+    lines = wl.conv_states.shape[0]
+    wide = np.random.default_rng(48).standard_normal((lines, 16, 6)).astype(np.float32)
+    wide[:, :, :3] = wl.conv_states
+    extra = wide[:, :, 3:].copy()
+    o = oracle.packed_causal_conv1d(wl.x, wl.dim, wl.weight, wl.bias, wide, wl.query_start_loc,
+                                    wl.cache_indices, wl.has_initial_state, wl.part_dim,
+                                    wl.activation, wl.null_block_id, lib=olib)
+    assert np.array_equal(o, o_ref)
+    assert np.array_equal(wide[:, :, :3].view(np.uint32), st_ref.view(np.uint32))
+    assert np.array_equal(wide[:, :, 3:], extra)
+
+
+def test_dim_first_state_equals_contiguous(olib):
+    """The state stored as (lines, 3, dim) and passed through its strides gives the
+    same outputs and the same updated values as the (lines, dim, 3) layout."""
+    wl = make_workload([5, 2, 9, 1], dim=16, part_dim=8, seed=49, init=[True, False, True, True])
+    o_ref, st_ref = oracle.run_workload(wl, lib=olib)
+    first = np.ascontiguousarray(wl.conv_states.transpose(0, 2, 1))  # (lines, 3, dim)
+    view = first.transpose(0, 2, 1)  # logical (lines, dim, 3), strides (3 dim, 1, dim)
+    o = oracle.packed_causal_conv1d(wl.x, wl.dim, wl.weight, wl.bias, view, wl.query_start_loc,
+                                    wl.cache_indices, wl.has_initial_state, wl.part_dim,
+                                    wl.activation, wl.null_block_id, lib=olib)
+    assert np.array_equal(o, o_ref)
+    assert np.array_equal(first.transpose(0, 2, 1).view(np.uint32), st_ref.view(np.uint32))
