@@ -126,6 +126,54 @@ def time_config(kd, torch, wl, steps: int, warmup: int, sets: int = 2):
     }
 
 
+def time_decode(kd, torch, wl, steps: int, warmup: int, sets: int = 4):
+    """Per-launch HIP-event times of the decode entry point on a decode batch (one
+    token per sequence, history from the stored lines)."""
+    dev = torch.device("cuda:0")
+    P = wl.dim // wl.part_dim
+    xb = x_tensor(torch, wl, dev)
+    bufs = []
+    for i in range(sets):
+        x = xb.clone() if i else xb
+        bufs.append(dict(
+            x=x[:, : wl.dim],
+            st=torch.from_numpy(wl.conv_states.copy()).to(dev),
+            out=torch.empty((P, wl.num_tokens, wl.part_dim), dtype=xb.dtype, device=dev),
+        ))
+    w = torch.from_numpy(wl.weight).to(dev)
+    b = None if wl.bias is None else torch.from_numpy(wl.bias).to(dev)
+    ci = torch.from_numpy(wl.cache_indices).to(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        s = bufs[i % sets]
+        kd.packed_causal_conv1d_update(s["x"], w, b, s["st"], ci, wl.part_dim, wl.activation,
+                                       wl.null_block_id, out=s["out"])
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize(dev)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for i, (a, z) in enumerate(evs):
+        a.record(stream)
+        step(i)
+        z.record(stream)
+    torch.cuda.synchronize(dev)
+    us = np.array([a.elapsed_time(z) for a, z in evs]) * 1e3
+    med = float(np.median(us))
+    nbytes = wl.algorithmic_bytes()
+    return {
+        "workload": wl.name,
+        "algorithmic_bytes": nbytes,
+        "kernel_us_median": round(med, 3),
+        "kernel_us_p10_p90": [round(float(np.percentile(us, 10)), 3),
+                              round(float(np.percentile(us, 90)), 3)],
+        "GB/s": round(nbytes / med / 1e3, 1),
+        "pct_of_peak": round(100.0 * nbytes / med / 1e3 / PEAK_HBM_GBS, 2),
+    }
+
+
 def cpu_baseline(wl, runs: int):
     import oracle
 
@@ -275,6 +323,11 @@ def main() -> int:
         result["other_configs"] = {
             str(k): time_config(kd, torch, workloads.CONFIGS[k](), steps=100, warmup=10)
             for k in (1, 2, 4, 5)
+        }
+        # Decode steps (one token per sequence) on the same channels.
+        result["decode"] = {
+            str(bsz): time_decode(kd, torch, workloads.decode_batch(bsz), steps=100, warmup=10)
+            for bsz in (64, 256, 1024)
         }
         # The same 16K-token workload with fp16 and FP32 x (output in x's format).
         result["other_formats"] = {

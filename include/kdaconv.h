@@ -130,6 +130,47 @@ int kdaconv_packed_causal_conv1d(
     void* out, kdaconv_stream_t stream);
 
 /*
+ * The decode step: the packed causal conv1d update of one token per sequence
+ * (page "vllm.models.kimi_k3.amd.ops.kda_decode": the first of the three steps its
+ * fused decode kernel replaces), with the FP32 state of the prefill op. Sequence b
+ * of the batch owns row b of x. Its result is that of kdaconv_packed_causal_conv1d
+ * on the same x with query_start_loc = {0, 1, ..., batch} and every
+ * has_initial_state set: the history is the stored line (zeros for the null block,
+ * whose line is neither read nor written), out[c / part_dim][b][c % part_dim] is the
+ * activated, rounded tap sum, and the line becomes entries 1, 2 and the new token.
+ * With an FP32 state the arithmetic is FP32 for every x dtype (page
+ * "vllm.models.kimi_k3.nvidia.ops.kda_conv", packed_causal_conv1d_supported's note).
+ * The bf16 state of that page's decode kernel is not supported.
+ *
+ * x                  elements of format dtype, (batch, dim) at row stride
+ *                    x_row_stride (16-byte aligned rows, as for the prefill op).
+ * weight, bias,
+ * conv_states,
+ * cache_indices,
+ * part_dim,
+ * activation,
+ * has_null_block,
+ * null_block_id      as for kdaconv_packed_causal_conv1d; cache_indices has one
+ *                    entry per sequence of the batch.
+ * out                elements of format dtype, dense (dim / part_dim, batch, part_dim),
+ *                    16-byte aligned.
+ *
+ * Precondition (not checked): live lines distinct within the batch.
+ * batch == 0 or dim == 0 returns KDACONV_OK with no launch. Status codes and
+ * their checks are those of kdaconv_packed_causal_conv1d, with batch in place of
+ * num_tokens and num_seqs.
+ */
+int kdaconv_packed_causal_conv1d_update(
+    const void* x, int dtype, int64_t batch, int64_t dim, int64_t x_row_stride,
+    const float* weight, int64_t weight_stride0, int64_t weight_stride1,
+    const float* bias,
+    float* conv_states, int64_t num_cache_lines,
+    int64_t cs_stride0, int64_t cs_stride1, int64_t cs_stride2,
+    const int32_t* cache_indices, int64_t cache_indices_stride,
+    int64_t part_dim, int activation, int has_null_block, int64_t null_block_id,
+    void* out, kdaconv_stream_t stream);
+
+/*
  * Host-only check of the same arguments (page: packed_causal_conv1d_supported):
  * returns the status kdaconv_packed_causal_conv1d would return before launching.
  * Pointers are only compared with NULL and tested for alignment, never

@@ -215,6 +215,26 @@ def packed_causal_conv1d(x: np.ndarray, dim: int, weight: np.ndarray, bias: Opti
     return out
 
 
+def packed_causal_conv1d_update(x: np.ndarray, dim: int, weight: np.ndarray,
+                                bias: Optional[np.ndarray], conv_states: np.ndarray,
+                                cache_indices: np.ndarray, part_dim: int, activation="silu",
+                                null_block_id: Optional[int] = None,
+                                out: Optional[np.ndarray] = None, lib=None,
+                                x_dtype: str = "bf16") -> np.ndarray:
+    """The decode step: row b of x is the one token of sequence b, whose history is
+    its stored line. With the FP32 state this is the operation itself at one token
+    per sequence with every initial-state flag set (page vllm.models.kimi_k3.amd.ops.
+    kda_decode names the packed causal conv1d update as the decode step; the
+    arithmetic is the prefill page's), so it runs the same C routine.
+    ``conv_states`` is updated in place; returns (dim // part_dim, batch, part_dim)."""
+    batch = x.shape[0]
+    qsl = np.arange(batch + 1, dtype=np.int32)
+    init = np.ones(batch, dtype=bool)
+    return packed_causal_conv1d(x, dim, weight, bias, conv_states, qsl, cache_indices, init,
+                                part_dim, activation, null_block_id, out=out, lib=lib,
+                                x_dtype=x_dtype)
+
+
 def run_workload(wl, out: Optional[np.ndarray] = None, lib=None):
     """Run the oracle on a ``workloads.Workload``; returns (out, updated conv_states copy)."""
     st = wl.conv_states.copy()

@@ -19,6 +19,7 @@ from . import _lib
 __all__ = [
     "NULL_BLOCK_ID",
     "packed_causal_conv1d_fn",
+    "packed_causal_conv1d_update",
     "packed_causal_conv1d_supported",
     "activation_map",
     "library_path",
@@ -80,7 +81,7 @@ def _conv_args(x, weight, bias, conv_states, query_start_loc, cache_indices, has
     ]
 
 
-def _check_tensors(x, weight, bias, conv_states, query_start_loc, cache_indices, has_initial_state):
+def _check_common(x, weight, bias, conv_states, cache_indices, num_seqs):
     if not x.is_cuda:
         raise ValueError("x must be a GPU tensor")
     _dtype_code(x.dtype)
@@ -93,22 +94,29 @@ def _check_tensors(x, weight, bias, conv_states, query_start_loc, cache_indices,
                              or not bias.is_contiguous()):
         raise ValueError("bias must be a contiguous float32 (dim,) tensor or None")
     if conv_states.dtype != torch.float32 or conv_states.dim() != 3 or conv_states.size(1) != dim:
-        raise ValueError("conv_states must be float32 of shape (cache lines, dim, 3)")
+        raise ValueError("conv_states must be float32 of shape (cache lines, dim, >= 3)")
     if conv_states.size(2) < 3:
         raise ValueError("conv_states needs at least 3 history entries per channel")
+    if cache_indices.dtype != torch.int32 or cache_indices.dim() != 1 or cache_indices.numel() < num_seqs:
+        raise ValueError("cache_indices must be a 1-D int32 tensor with one entry per sequence")
+    for t in (weight, bias, conv_states, cache_indices):
+        if t is not None and t.device != x.device:
+            raise ValueError("all tensors must be on the device of x")
+
+
+def _check_tensors(x, weight, bias, conv_states, query_start_loc, cache_indices, has_initial_state):
     if query_start_loc.dtype != torch.int32 or query_start_loc.dim() != 1:
         raise ValueError("query_start_loc must be a 1-D int32 tensor")
     if not query_start_loc.is_contiguous():
         raise ValueError("query_start_loc must be contiguous")
     num_seqs = query_start_loc.numel() - 1
-    if cache_indices.dtype != torch.int32 or cache_indices.dim() != 1 or cache_indices.numel() < num_seqs:
-        raise ValueError("cache_indices must be a 1-D int32 tensor with one entry per sequence")
+    _check_common(x, weight, bias, conv_states, cache_indices, num_seqs)
     if has_initial_state is not None:
         if has_initial_state.dtype not in (torch.bool, torch.uint8) or not has_initial_state.is_contiguous():
             raise ValueError("has_initial_state must be a contiguous bool tensor or None")
         if has_initial_state.numel() < num_seqs:
             raise ValueError("has_initial_state needs one entry per sequence")
-    for t in (weight, bias, conv_states, query_start_loc, cache_indices, has_initial_state):
+    for t in (query_start_loc, has_initial_state):
         if t is not None and t.device != x.device:
             raise ValueError("all tensors must be on the device of x")
 
@@ -158,6 +166,54 @@ def packed_causal_conv1d_fn(
     with torch.cuda.device(x.device):
         rc = lib.kdaconv_packed_causal_conv1d(*args, _stream_handle(x.device))
     _lib.check(rc, "packed_causal_conv1d_fn")
+    return out
+
+
+def packed_causal_conv1d_update(
+    x: torch.Tensor,
+    weight: torch.Tensor,
+    bias: Optional[torch.Tensor],
+    conv_states: torch.Tensor,
+    cache_indices: torch.Tensor,
+    part_dim: int,
+    activation="silu",
+    null_block_id: Optional[int] = NULL_BLOCK_ID,
+    out: Optional[torch.Tensor] = None,
+) -> torch.Tensor:
+    """Decode step: one token per sequence, row b of x (batch, dim) for sequence b.
+
+    The packed causal conv1d update of page vllm.models.kimi_k3.amd.ops.kda_decode
+    with the FP32 state of packed_causal_conv1d_fn: the result equals that function
+    with query_start_loc = [0, 1, ..., batch] and every has_initial_state true. The
+    state lines named by cache_indices shift by one token in place (the null
+    block's line is neither read nor written). Returns (dim // part_dim, batch,
+    part_dim) in x's dtype. Queued on the current stream; no synchronisation.
+    """
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D (batch, dim)")
+    batch, dim = x.shape
+    if part_dim <= 0 or dim % part_dim != 0:
+        raise ValueError(f"dim {dim} is not a multiple of part_dim {part_dim}")
+    shape = (dim // part_dim, batch, part_dim)
+    if out is None:
+        out = torch.empty(shape, dtype=x.dtype, device=x.device)
+    elif tuple(out.shape) != shape or out.dtype != x.dtype or not out.is_contiguous() or out.device != x.device:
+        raise ValueError(f"out must be a contiguous {x.dtype} tensor of shape {shape} on {x.device}")
+    if batch == 0:
+        return out
+    _check_common(x, weight, bias, conv_states, cache_indices, batch)
+    lib = _lib.load()
+    with torch.cuda.device(x.device):
+        rc = lib.kdaconv_packed_causal_conv1d_update(
+            _ptr(x), _dtype_code(x.dtype), batch, dim, x.stride(0),
+            _ptr(weight), weight.stride(0), weight.stride(1), _ptr(bias),
+            _ptr(conv_states), conv_states.size(0),
+            conv_states.stride(0), conv_states.stride(1), conv_states.stride(2),
+            _ptr(cache_indices), cache_indices.stride(0),
+            int(part_dim), _activation_code(activation),
+            int(null_block_id is not None), 0 if null_block_id is None else int(null_block_id),
+            _ptr(out), _stream_handle(x.device))
+    _lib.check(rc, "packed_causal_conv1d_update")
     return out
 
 

@@ -14,6 +14,7 @@ BF16, F16, F32 = 0, 1, 2
 # Every entry point include/kdaconv.h declares.
 EXPORTS = (
     "kdaconv_packed_causal_conv1d",
+    "kdaconv_packed_causal_conv1d_update",
     "kdaconv_validate",
     "kdaconv_activation_map",
     "kdaconv_status_string",
@@ -49,6 +50,15 @@ def load() -> ctypes.CDLL:
     ]
     lib.kdaconv_packed_causal_conv1d.argtypes = conv_args + [vp]
     lib.kdaconv_packed_causal_conv1d.restype = i32
+    lib.kdaconv_packed_causal_conv1d_update.argtypes = [
+        vp, i32, i64, i64, i64,  # x, dtype, batch, dim, x_row_stride
+        vp, i64, i64, vp,  # weight, weight strides, bias
+        vp, i64, i64, i64, i64,  # conv_states, num_cache_lines, strides
+        vp, i64,  # cache_indices, stride
+        i64, i32, i32, i64,  # part_dim, activation, has_null_block, null_block_id
+        vp, vp,  # out, stream
+    ]
+    lib.kdaconv_packed_causal_conv1d_update.restype = i32
     lib.kdaconv_validate.argtypes = conv_args
     lib.kdaconv_validate.restype = i32
     lib.kdaconv_activation_map.argtypes = [ctypes.c_uint32, i64, i32, i32, vp, vp]

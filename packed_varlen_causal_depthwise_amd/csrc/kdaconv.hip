@@ -303,6 +303,146 @@ struct ConvWorker {
     }
   }
 
+  // The lane's V channels of state line `line`: h0, h1, h2 = entries 0, 1, 2.
+  __device__ __forceinline__ void load_state(int64_t line, float (&h0)[V], float (&h1)[V],
+                                             float (&h2)[V]) const {
+    const float* sp = P.states + line * P.cs_stride0;
+    if (P.state_vec) {
+      // The lane's V channels x 3 values are 3V consecutive floats.
+      const __amdgpu_buffer_rsrc_t sr = make_rsrc(sp);
+      float f[3 * V];
+#pragma unroll
+      for (int i = 0; i < 3 * V / 4; ++i) {
+        const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(sr, (uint32_t)cl * 12u + 16u * i, 0, kKeep);
+        f[4 * i] = __uint_as_float(t[0]);
+        f[4 * i + 1] = __uint_as_float(t[1]);
+        f[4 * i + 2] = __uint_as_float(t[2]);
+        f[4 * i + 3] = __uint_as_float(t[3]);
+      }
+#pragma unroll
+      for (int k = 0; k < V; ++k) {
+        h0[k] = f[3 * k];
+        h1[k] = f[3 * k + 1];
+        h2[k] = f[3 * k + 2];
+      }
+    } else if (P.state_rows) {
+      // History k of the lane's V channels: V consecutive floats of row k.
+      const __amdgpu_buffer_rsrc_t sr = make_rsrc(sp);
+      const uint32_t row = (uint32_t)P.cs_stride2 * 4u;
+#pragma unroll
+      for (int i = 0; i < V / 4; ++i) {
+        const uint32_t o = (uint32_t)(cl + 4 * i) * 4u;
+        const u32x4 t0 = __builtin_amdgcn_raw_buffer_load_b128(sr, o, 0, kKeep);
+        const u32x4 t1 = __builtin_amdgcn_raw_buffer_load_b128(sr, o + row, 0, kKeep);
+        const u32x4 t2 = __builtin_amdgcn_raw_buffer_load_b128(sr, o + 2 * row, 0, kKeep);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          h0[4 * i + k] = __uint_as_float(t0[k]);
+          h1[4 * i + k] = __uint_as_float(t1[k]);
+          h2[4 * i + k] = __uint_as_float(t2[k]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < V; ++k) {
+        const float* cp = sp + (int64_t)(cl + k) * P.cs_stride1;
+        h0[k] = cp[0];
+        h1[k] = cp[P.cs_stride2];
+        h2[k] = cp[2 * P.cs_stride2];
+      }
+    }
+  }
+
+  // Writes entries 0, 1, 2 of the lane's V channels of line `line`.
+  __device__ __forceinline__ void store_state(int64_t line, const float (&h0)[V],
+                                              const float (&h1)[V], const float (&h2)[V]) const {
+    float* sp = P.states + line * P.cs_stride0;
+    if (P.state_vec) {
+      float f[3 * V];
+#pragma unroll
+      for (int k = 0; k < V; ++k) {
+        f[3 * k] = h0[k];
+        f[3 * k + 1] = h1[k];
+        f[3 * k + 2] = h2[k];
+      }
+      float4* sv = reinterpret_cast<float4*>(sp + (int64_t)cl * 3);
+#pragma unroll
+      for (int i = 0; i < 3 * V / 4; ++i)
+        sv[i] = make_float4(f[4 * i], f[4 * i + 1], f[4 * i + 2], f[4 * i + 3]);
+    } else if (P.state_rows) {
+#pragma unroll
+      for (int i = 0; i < V / 4; ++i) {
+        float* cp = sp + cl + 4 * i;
+        *reinterpret_cast<float4*>(cp) = make_float4(h0[4 * i], h0[4 * i + 1], h0[4 * i + 2], h0[4 * i + 3]);
+        *reinterpret_cast<float4*>(cp + P.cs_stride2) =
+            make_float4(h1[4 * i], h1[4 * i + 1], h1[4 * i + 2], h1[4 * i + 3]);
+        *reinterpret_cast<float4*>(cp + 2 * P.cs_stride2) =
+            make_float4(h2[4 * i], h2[4 * i + 1], h2[4 * i + 2], h2[4 * i + 3]);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < V; ++k) {
+        float* cp = sp + (int64_t)(cl + k) * P.cs_stride1;
+        cp[0] = h0[k];
+        cp[P.cs_stride2] = h1[k];
+        cp[2 * P.cs_stride2] = h2[k];
+      }
+    }
+  }
+
+  // Decode step of sequence s, whose one token is row s of x: history from the
+  // stored line (zeros for the null block), one output row, the line shifted by one
+  // token. The elements that need the exact path get their exact words before the
+  // row is stored, so nothing is written twice.
+  __device__ __forceinline__ void decode(int s) {
+    const int64_t line = P.cache_indices[(int64_t)s * P.ci_stride];
+    const bool live = !(P.has_null_block && line == P.null_block_id) && line >= 0 &&
+                      line < P.num_cache_lines;
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(P.x + (int64_t)s * P.x_row_stride * kBytes);
+    float xv[V], h0[V], h1[V], h2[V];
+    unpack<kF, V>(L::template load<kStream>(xr, xvo, 0), xv);
+    if (live) {
+      load_state(line, h0, h1, h2);
+    } else {
+#pragma unroll
+      for (int k = 0; k < V; ++k) h0[k] = h1[k] = h2[k] = 0.0f;
+    }
+    float acc[1][V];
+#pragma unroll
+    for (int k = 0; k < V; ++k) {
+      float a = bs[k];
+      a = __builtin_fmaf(w0[k], h0[k], a);
+      a = __builtin_fmaf(w1[k], h1[k], a);
+      a = __builtin_fmaf(w2[k], h2[k], a);
+      a = __builtin_fmaf(w3[k], xv[k], a);
+      acc[0][k] = a;
+    }
+    constexpr int kWords = row_words<kF, V>();
+    uint32_t words[1][kWords];
+    float y[1][V];
+    uint32_t aux[1][V];
+    const bool check = activate_rows<kF, kSilu, V, 1>(acc, y, aux, words);
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(check) != 0, 0)) {
+#pragma unroll
+      for (int k = 0; k < V; ++k) {
+        if (needs_exact<kF, kSilu>(acc[0][k], y[0][k], aux[0][k])) {
+          const uint32_t wd = act_word_exact<kF>(acc[0][k], kSilu);
+          if (kBytes == 4)
+            words[0][k] = wd;
+          else if (k & 1)
+            words[0][k / 2] = (words[0][k / 2] & 0xFFFFu) | (wd << 16);
+          else
+            words[0][k / 2] = (words[0][k / 2] & 0xFFFF0000u) | wd;
+        }
+      }
+    }
+    vec o;
+#pragma unroll
+    for (int i = 0; i < kWords; ++i) o[i] = words[0][i];
+    L::template store<kStream>(o, orsrc, ovo, (uint32_t)s * orow_bytes);
+    if (live && active) store_state(line, h1, h2, xv);
+  }
+
   // Issues the loads of a valid tile's x rows: always 3 history rows (the first
   // row again when the tile has no history) and R tile rows (rows past the
   // tile's end repeat its last row), so the number of loads never depends on the
@@ -340,51 +480,7 @@ struct ConvWorker {
              line < P.num_cache_lines;
       const bool init = live && P.has_init != nullptr && P.has_init[d.s] != 0;
       if (init) {
-        const float* sp = P.states + line * P.cs_stride0;
-        if (P.state_vec) {
-          // The lane's V channels x 3 values are 3V consecutive floats.
-          const __amdgpu_buffer_rsrc_t sr = make_rsrc(sp);
-          float f[3 * V];
-#pragma unroll
-          for (int i = 0; i < 3 * V / 4; ++i) {
-            const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(sr, (uint32_t)cl * 12u + 16u * i, 0, kKeep);
-            f[4 * i] = __uint_as_float(t[0]);
-            f[4 * i + 1] = __uint_as_float(t[1]);
-            f[4 * i + 2] = __uint_as_float(t[2]);
-            f[4 * i + 3] = __uint_as_float(t[3]);
-          }
-#pragma unroll
-          for (int k = 0; k < V; ++k) {
-            h0[k] = f[3 * k];
-            h1[k] = f[3 * k + 1];
-            h2[k] = f[3 * k + 2];
-          }
-        } else if (P.state_rows) {
-          // History k of the lane's V channels: V consecutive floats of row k.
-          const __amdgpu_buffer_rsrc_t sr = make_rsrc(sp);
-          const uint32_t row = (uint32_t)P.cs_stride2 * 4u;
-#pragma unroll
-          for (int i = 0; i < V / 4; ++i) {
-            const uint32_t o = (uint32_t)(cl + 4 * i) * 4u;
-            const u32x4 t0 = __builtin_amdgcn_raw_buffer_load_b128(sr, o, 0, kKeep);
-            const u32x4 t1 = __builtin_amdgcn_raw_buffer_load_b128(sr, o + row, 0, kKeep);
-            const u32x4 t2 = __builtin_amdgcn_raw_buffer_load_b128(sr, o + 2 * row, 0, kKeep);
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              h0[4 * i + k] = __uint_as_float(t0[k]);
-              h1[4 * i + k] = __uint_as_float(t1[k]);
-              h2[4 * i + k] = __uint_as_float(t2[k]);
-            }
-          }
-        } else {
-#pragma unroll
-          for (int k = 0; k < V; ++k) {
-            const float* cp = sp + (int64_t)(cl + k) * P.cs_stride1;
-            h0[k] = cp[0];
-            h1[k] = cp[P.cs_stride2];
-            h2[k] = cp[2 * P.cs_stride2];
-          }
-        }
+        load_state(line, h0, h1, h2);
       } else {
 #pragma unroll
         for (int k = 0; k < V; ++k) h0[k] = h1[k] = h2[k] = 0.0f;
@@ -471,38 +567,7 @@ struct ConvWorker {
         unpack<kF, V>(L::template load<kKeep>(tr, xvo, xrow_bytes), h1);
         unpack<kF, V>(L::template load<kKeep>(tr, xvo, 2 * xrow_bytes), h2);
       }
-      float* sp = P.states + line * P.cs_stride0;
-      if (P.state_vec) {
-        float f[3 * V];
-#pragma unroll
-        for (int k = 0; k < V; ++k) {
-          f[3 * k] = h0[k];
-          f[3 * k + 1] = h1[k];
-          f[3 * k + 2] = h2[k];
-        }
-        float4* sv = reinterpret_cast<float4*>(sp + (int64_t)cl * 3);
-#pragma unroll
-        for (int i = 0; i < 3 * V / 4; ++i)
-          sv[i] = make_float4(f[4 * i], f[4 * i + 1], f[4 * i + 2], f[4 * i + 3]);
-      } else if (P.state_rows) {
-#pragma unroll
-        for (int i = 0; i < V / 4; ++i) {
-          float* cp = sp + cl + 4 * i;
-          *reinterpret_cast<float4*>(cp) = make_float4(h0[4 * i], h0[4 * i + 1], h0[4 * i + 2], h0[4 * i + 3]);
-          *reinterpret_cast<float4*>(cp + P.cs_stride2) =
-              make_float4(h1[4 * i], h1[4 * i + 1], h1[4 * i + 2], h1[4 * i + 3]);
-          *reinterpret_cast<float4*>(cp + 2 * P.cs_stride2) =
-              make_float4(h2[4 * i], h2[4 * i + 1], h2[4 * i + 2], h2[4 * i + 3]);
-        }
-      } else {
-#pragma unroll
-        for (int k = 0; k < V; ++k) {
-          float* cp = sp + (int64_t)(cl + k) * P.cs_stride1;
-          cp[0] = h0[k];
-          cp[P.cs_stride2] = h1[k];
-          cp[2 * P.cs_stride2] = h2[k];
-        }
-      }
+      store_state(line, h0, h1, h2);
     }
   }
 
@@ -545,6 +610,21 @@ __global__ __launch_bounds__(kWave * kG) __attribute__((amdgpu_waves_per_eu(kMin
   w.issue(buf, d);
   w.compute(buf, d);
   w.finish();
+}
+
+// Decode update: program p is sequence p (row p of x), one wave per column block,
+// kG column blocks per workgroup. No search: every sequence has exactly one token.
+template <int kF, int V, int kG, bool kBias, bool kSilu>
+__global__ __launch_bounds__(kWave * kG) void packed_conv_update_kernel(const ConvParams P) {
+  const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
+  const uint32_t groups = ((uint32_t)P.col_blocks + kG - 1) / kG;
+  const int p = (int)(blockIdx.x / groups);
+  const int cb = (int)(blockIdx.x - (uint32_t)p * groups) * kG + wave;
+  if (cb >= P.col_blocks) return;
+  ConvWorker<kF, V, 1, kBias, kSilu> w(P, lane, cb, nullptr);
+  w.load_weights();
+  w.decode(p);
 }
 
 // The activation map on consecutive FP32 bit patterns, 8 per lane as two rows of 4,
@@ -663,6 +743,87 @@ void launch(ConvParams P, int64_t cols, bool bias, bool silu, hipStream_t st) {
     launch_group<kF, V, 1>(P, bias, silu, st);
 }
 
+template <int kF, int V, int kG>
+void launch_update_group(const ConvParams& P, bool bias, bool silu, hipStream_t st) {
+  const uint64_t groups = ((uint64_t)P.col_blocks + kG - 1) / kG;
+  const dim3 grid((unsigned)((uint64_t)P.programs * groups));
+  const dim3 block(kWave * kG);
+  if (bias) {
+    if (silu)
+      hipLaunchKernelGGL((packed_conv_update_kernel<kF, V, kG, true, true>), grid, block, 0, st, P);
+    else
+      hipLaunchKernelGGL((packed_conv_update_kernel<kF, V, kG, true, false>), grid, block, 0, st, P);
+  } else {
+    if (silu)
+      hipLaunchKernelGGL((packed_conv_update_kernel<kF, V, kG, false, true>), grid, block, 0, st, P);
+    else
+      hipLaunchKernelGGL((packed_conv_update_kernel<kF, V, kG, false, false>), grid, block, 0, st, P);
+  }
+}
+
+template <int kF, int V>
+void launch_update(ConvParams P, int64_t cols, bool bias, bool silu, hipStream_t st) {
+  P.col_blocks = (int32_t)((cols / V + kWave - 1) / kWave);
+  P.programs = P.num_seqs;
+  if (P.col_blocks % 2 == 0)
+    launch_update_group<kF, V, 2>(P, bias, silu, st);
+  else
+    launch_update_group<kF, V, 1>(P, bias, silu, st);
+}
+
+// Fields of ConvParams shared by both operations.
+void fill_common(ConvParams& P, const void* x, int64_t num_tokens, int64_t x_row_stride,
+                 const float* weight, int64_t ws0, int64_t ws1, const float* bias,
+                 float* conv_states, int64_t num_cache_lines, int64_t cs0, int64_t cs1, int64_t cs2,
+                 const int32_t* cache_indices, int64_t ci_stride, int64_t dim, int64_t part_dim,
+                 int has_null_block, int64_t null_block_id) {
+  P.x = static_cast<const char*>(x);
+  P.weight = weight;
+  P.bias = bias;
+  P.states = conv_states;
+  P.qsl = nullptr;
+  P.cache_indices = cache_indices;
+  P.has_init = nullptr;
+  P.x_row_stride = x_row_stride;
+  P.w_stride0 = ws0;
+  P.w_stride1 = ws1;
+  P.cs_stride0 = cs0;
+  P.cs_stride1 = cs1;
+  P.cs_stride2 = cs2;
+  P.ci_stride = ci_stride;
+  P.num_cache_lines = num_cache_lines;
+  P.plane_stride = num_tokens * part_dim;
+  P.null_block_id = null_block_id;
+  P.num_tokens = (int32_t)num_tokens;
+  P.part_dim = (int32_t)part_dim;
+  P.search_levels = 0;
+  P.search_top = 1;
+  P.has_null_block = has_null_block != 0;
+  P.weight_vec = ws0 == 4 && ws1 == 1 && aligned16(weight);
+  P.bias_vec = bias != nullptr && aligned16(bias);
+  P.state_vec = cs1 == 3 && cs2 == 1 && cs0 % 4 == 0 && aligned16(conv_states);
+  P.state_rows = cs1 == 1 && cs2 >= dim && cs2 % 4 == 0 && cs0 % 4 == 0 &&
+                 aligned16(conv_states) && (2 * cs2 + dim) * 4 < INT32_MAX;
+}
+
+// Launches op(P, cols) over groups of whole planes small enough that a lane's offset
+// into the group's output (planes * num_tokens * part_dim * element bytes) stays
+// below 2^31. One launch in every realistic case.
+template <class Op>
+void for_plane_groups(ConvParams& P, int64_t num_tokens, int64_t dim, int64_t part_dim,
+                      int64_t eb, void* out, Op op) {
+  const int64_t plane_bytes = num_tokens * part_dim * eb;
+  const int64_t planes = dim / part_dim;
+  const int64_t per_launch = plane_bytes > 0 ? std::max<int64_t>(1, INT32_MAX / plane_bytes) : planes;
+  for (int64_t pl = 0; pl < planes; pl += per_launch) {
+    const int64_t pe = std::min(planes, pl + per_launch);
+    P.col_begin = (int32_t)(pl * part_dim);
+    P.col_end = (int32_t)(pe * part_dim);
+    P.out = static_cast<char*>(out) + pl * P.plane_stride * eb;
+    op(P, (pe - pl) * part_dim);
+  }
+}
+
 }  // namespace
 }  // namespace kdaconv
 
@@ -706,26 +867,12 @@ extern "C" int kdaconv_packed_causal_conv1d(
 
   const int64_t eb = dtype_bytes(dtype);
   ConvParams P;
-  P.x = static_cast<const char*>(x);
-  P.weight = weight;
-  P.bias = bias;
-  P.states = conv_states;
+  fill_common(P, x, num_tokens, x_row_stride, weight, weight_stride0, weight_stride1, bias,
+              conv_states, num_cache_lines, cs_stride0, cs_stride1, cs_stride2, cache_indices,
+              cache_indices_stride, dim, part_dim, has_null_block, null_block_id);
   P.qsl = query_start_loc;
-  P.cache_indices = cache_indices;
   P.has_init = has_initial_state;
-  P.x_row_stride = x_row_stride;
-  P.w_stride0 = weight_stride0;
-  P.w_stride1 = weight_stride1;
-  P.cs_stride0 = cs_stride0;
-  P.cs_stride1 = cs_stride1;
-  P.cs_stride2 = cs_stride2;
-  P.ci_stride = cache_indices_stride;
-  P.num_cache_lines = num_cache_lines;
-  P.plane_stride = num_tokens * part_dim;
-  P.null_block_id = null_block_id;
-  P.num_tokens = (int32_t)num_tokens;
   P.num_seqs = (int32_t)num_seqs;
-  P.part_dim = (int32_t)part_dim;
   int levels = 0;
   int64_t reach = 1;
   while (reach < num_seqs) {
@@ -734,34 +881,63 @@ extern "C" int kdaconv_packed_causal_conv1d(
   }
   P.search_levels = levels;
   P.search_top = (int32_t)(levels > 0 ? reach / kWave : 1);
-  P.has_null_block = has_null_block != 0;
-  P.weight_vec = weight_stride0 == 4 && weight_stride1 == 1 && aligned16(weight);
-  P.bias_vec = bias != nullptr && aligned16(bias);
-  P.state_vec = cs_stride1 == 3 && cs_stride2 == 1 && cs_stride0 % 4 == 0 && aligned16(conv_states);
-  P.state_rows = cs_stride1 == 1 && cs_stride2 >= dim && cs_stride2 % 4 == 0 && cs_stride0 % 4 == 0 &&
-                 aligned16(conv_states) && (2 * cs_stride2 + dim) * 4 < INT32_MAX;
 
-  // Launches cover groups of whole planes small enough that a lane's offset
-  // into the group's output (planes * num_tokens * part_dim * element bytes)
-  // stays below 2^31. One launch in every realistic case.
-  const int64_t plane_bytes = num_tokens * part_dim * eb;
-  const int64_t planes = dim / part_dim;
-  const int64_t per_launch = plane_bytes > 0 ? std::max<int64_t>(1, INT32_MAX / plane_bytes) : planes;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const bool silu = activation == KDACONV_ACT_SILU;
-  for (int64_t pl = 0; pl < planes; pl += per_launch) {
-    const int64_t pe = std::min(planes, pl + per_launch);
-    P.col_begin = (int32_t)(pl * part_dim);
-    P.col_end = (int32_t)(pe * part_dim);
-    P.out = static_cast<char*>(out) + pl * P.plane_stride * eb;
-    const int64_t cols = (pe - pl) * part_dim;
+  const bool has_bias = bias != nullptr;
+  for_plane_groups(P, num_tokens, dim, part_dim, eb, out, [&](ConvParams& Q, int64_t cols) {
     if (dtype == kF32)
-      launch<kF32, kLaneChannels>(P, cols, bias != nullptr, silu, st);
+      launch<kF32, kLaneChannels>(Q, cols, has_bias, silu, st);
     else if (dtype == kF16)
-      launch<kF16, kLaneChannels>(P, cols, bias != nullptr, silu, st);
+      launch<kF16, kLaneChannels>(Q, cols, has_bias, silu, st);
     else
-      launch<kBF16, kLaneChannels>(P, cols, bias != nullptr, silu, st);
-  }
+      launch<kBF16, kLaneChannels>(Q, cols, has_bias, silu, st);
+  });
+  return hipGetLastError() == hipSuccess ? KDACONV_OK : KDACONV_ELAUNCH;
+}
+
+extern "C" int kdaconv_packed_causal_conv1d_update(
+    const void* x, int dtype, int64_t batch, int64_t dim, int64_t x_row_stride,
+    const float* weight, int64_t weight_stride0, int64_t weight_stride1, const float* bias,
+    float* conv_states, int64_t num_cache_lines, int64_t cs_stride0, int64_t cs_stride1,
+    int64_t cs_stride2, const int32_t* cache_indices, int64_t cache_indices_stride,
+    int64_t part_dim, int activation, int has_null_block, int64_t null_block_id, void* out,
+    kdaconv_stream_t stream) {
+  if (batch < 0 || dim < 0 || num_cache_lines < 0) return KDACONV_EINVAL;
+  if (!known_dtype(dtype)) return KDACONV_EINVAL;
+  if (part_dim <= 0 || dim % part_dim != 0) return KDACONV_EINVAL;
+  if (x_row_stride < dim) return KDACONV_EINVAL;
+  if (activation != KDACONV_ACT_NONE && activation != KDACONV_ACT_SILU) return KDACONV_EINVAL;
+  const int64_t eb = dtype_bytes(dtype);
+  if (part_dim % 8 != 0 || (x_row_stride * eb) % 16 != 0) return KDACONV_EUNSUPPORTED;
+  if (weight_stride0 < 0 || weight_stride1 < 0 || cs_stride0 < 0 || cs_stride1 < 0 ||
+      cs_stride2 < 0 || cache_indices_stride < 0)
+    return KDACONV_EUNSUPPORTED;
+  if (batch > INT32_MAX - 1 || dim > INT32_MAX / 2) return KDACONV_EUNSUPPORTED;
+  if (batch * ((dim + kWave * kLaneChannels - 1) / (kWave * kLaneChannels)) > INT32_MAX)
+    return KDACONV_EUNSUPPORTED;
+  if (batch * part_dim * eb > INT32_MAX / 2) return KDACONV_EUNSUPPORTED;
+  if (dim * cs_stride1 * 4 > INT32_MAX) return KDACONV_EUNSUPPORTED;
+  if (batch == 0 || dim == 0) return KDACONV_OK;
+  if (!x || !weight || !conv_states || !cache_indices || !out) return KDACONV_EINVAL;
+  if (!aligned16(x) || !aligned16(out)) return KDACONV_EUNSUPPORTED;
+
+  ConvParams P;
+  fill_common(P, x, batch, x_row_stride, weight, weight_stride0, weight_stride1, bias,
+              conv_states, num_cache_lines, cs_stride0, cs_stride1, cs_stride2, cache_indices,
+              cache_indices_stride, dim, part_dim, has_null_block, null_block_id);
+  P.num_seqs = (int32_t)batch;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const bool silu = activation == KDACONV_ACT_SILU;
+  const bool has_bias = bias != nullptr;
+  for_plane_groups(P, batch, dim, part_dim, eb, out, [&](ConvParams& Q, int64_t cols) {
+    if (dtype == kF32)
+      launch_update<kF32, kLaneChannels>(Q, cols, has_bias, silu, st);
+    else if (dtype == kF16)
+      launch_update<kF16, kLaneChannels>(Q, cols, has_bias, silu, st);
+    else
+      launch_update<kBF16, kLaneChannels>(Q, cols, has_bias, silu, st);
+  });
   return hipGetLastError() == hipSuccess ? KDACONV_OK : KDACONV_ELAUNCH;
 }
 

@@ -125,3 +125,34 @@ def test_missing_library_fails_loudly(tmp_path, monkeypatch):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(_lib.LibraryMissing):
         _lib.load()
+
+
+def _update_args(**kw):
+    a = dict(x=A, dt=_lib.BF16, B=64, dim=384, sx=384, w=A, ws0=4, ws1=1, b=A, st=A, lines=4,
+             cs0=1152, cs1=3, cs2=1, ci=A, cis=1, pd=128, act=1, hn=0, nid=0, out=A)
+    a.update(kw)
+    return [a["x"], a["dt"], a["B"], a["dim"], a["sx"], a["w"], a["ws0"], a["ws1"], a["b"],
+            a["st"], a["lines"], a["cs0"], a["cs1"], a["cs2"], a["ci"], a["cis"], a["pd"],
+            a["act"], a["hn"], a["nid"], a["out"], None]
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=-1), _lib.EINVAL),
+    (dict(dt=7), _lib.EINVAL),
+    (dict(pd=100), _lib.EINVAL),
+    (dict(sx=376), _lib.EINVAL),
+    (dict(act=3), _lib.EINVAL),
+    (dict(x=0), _lib.EINVAL),
+    (dict(ci=0), _lib.EINVAL),
+    (dict(out=0), _lib.EINVAL),
+    (dict(dim=96, sx=96, pd=12), _lib.EUNSUPPORTED),
+    (dict(sx=390), _lib.EUNSUPPORTED),
+    (dict(x=A + 2), _lib.EUNSUPPORTED),
+    (dict(out=A + 8), _lib.EUNSUPPORTED),
+    (dict(cs2=-1), _lib.EUNSUPPORTED),
+    (dict(B=0, x=0, out=0), _lib.OK),  # nothing to do: no launch
+])
+def test_update_status_codes(kw, code):
+    """Argument checks of the decode entry point (they run before any HIP call)."""
+    lib = _lib.load()
+    assert lib.kdaconv_packed_causal_conv1d_update(*_update_args(**kw)) == code

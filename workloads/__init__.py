@@ -250,6 +250,23 @@ def config5(seed: int = 5, x_dtype: str = "bf16") -> Workload:
                     x, dim, w, None, st, _qsl(lens), ci, init, 192, None, None, x_dtype)
 
 
+def decode_batch(batch: int = 256, seed: int = 6, x_dtype: str = "bf16") -> Workload:
+    """A decode step: ``batch`` sequences of one token each, dim 4608 (3 x 1536) in rows
+    of 9728, every sequence continuing from its stored line (1024 lines), bias, SiLU.
+    As a Workload its offsets are 0, 1, ..., batch and every initial-state flag is set,
+    which is what the decode entry point computes."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    dim, lines = 4608, 1024
+    x = _x_buffer(rng, batch, dim, IN_PROJ_ROW_STRIDE, x_dtype=x_dtype)
+    w = _normal(rng, (dim, 4), 0.5)
+    b = _normal(rng, (dim,), 0.1)
+    st = _normal(rng, (lines, dim, 3), 1.0)
+    ci = rng.permutation(lines)[:batch].astype(np.int32)
+    return Workload(f"decode: {batch} sequences x 1 token, dim 4608, part_dim 1536, stride 9728",
+                    x, dim, w, b, st, _qsl(np.ones(batch, dtype=np.int64)), ci,
+                    np.ones(batch, dtype=bool), 1536, "silu", None, x_dtype)
+
+
 CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}
 
 
