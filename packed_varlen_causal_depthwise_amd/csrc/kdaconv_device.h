@@ -90,49 +90,46 @@ __device__ __forceinline__ uint32_t word_exact(float y) {
 // --------------------------------------------------------------------------------------
 // Fast SiLU for the 16-bit formats.
 
-// Bound, in FP32 ulps (distance between bit patterns), on |fast SiLU - binary32 SiLU|
-// wherever the fast path is trusted. Fast values within this many ulps of a rounding
-// boundary of the output format are recomputed exactly.
-constexpr uint32_t kSiluUlpBound = 16;
-// The fast path is trusted while its exp2 result stays below 2048, which holds for
-// every a above about -7.6 (the product a * -log2(e) is rounded before the exp2, an
-// error that grows with |a|). Larger results, and NaN (either sign), are taken by
-// the exact path. Compared as bit patterns: exp2 never returns a negative number,
-// and every NaN pattern lies above the threshold.
-constexpr uint32_t kFastExpLimitBits = 0x45000000u;  // 2048.0f
+// Where the fast path is trusted, and how far from the binary32 SiLU it may be. The
+// error, in FP32 ulps (distance between bit patterns), comes from the rounded exp2
+// argument (about |a| * 2^-24 relative, so it grows with -a), the exp2 and
+// reciprocal approximations and two roundings. Measured on gfx950 over all 2^32
+// inputs: at most 3 ulps for a >= 0, 5 for -4 <= a < 0, 9 for -7.5 <= a < -4. The
+// bounds below keep one ulp to spare, and the exhaustive activation-map tests check
+// the resulting words on every input.
+//
+// Each format trades the width of the nearness window against how many accumulators
+// skip the fast path. bf16 drops 16 bits, so even a 10-ulp window is rare (0.03 % of
+// values) and the fast path is trusted down to a = -7.5. fp16 drops 13 bits, where a
+// 10-ulp window would send 0.26 % of values to the exact path; it trusts the fast
+// path only down to a = -4 and uses the 6-ulp bound that holds there.
+//
+//   silu_bound<kF>()      bound on the error where the fast path is trusted
+//   exact_below<kF>()     accumulators below it take the exact path
+//   fast_exp_limit<kF>()  row test for them: every a below exact_below has an exp2
+//                         result at or above this bit pattern (2048.0f: a < -7.6;
+//                         32.0f: a < -3.46), so a row whose largest exp2 result is
+//                         smaller holds none. NaN of either sign also lies above it:
+//                         exp2 never returns a negative number and every NaN
+//                         pattern is larger.
+template <int kF>
+constexpr uint32_t silu_bound() {
+  return kF == kF16 ? 6u : 10u;
+}
+template <int kF>
+constexpr float exact_below() {
+  return kF == kF16 ? -4.0f : -7.5f;
+}
+template <int kF>
+constexpr uint32_t fast_exp_limit() {
+  return kF == kF16 ? 0x42000000u : 0x45000000u;
+}
 
 // SiLU from the hardware exp2 and reciprocal; e receives the exp2 result, which
-// decides whether the value can be trusted (kFastExpLimitBits).
+// decides whether the value can be trusted (fast_exp_limit).
 __device__ __forceinline__ float silu_fast(float a, float& e) {
   e = __builtin_amdgcn_exp2f(a * -1.44269504088896341f);
   return a * __builtin_amdgcn_rcpf(1.0f + e);
-}
-
-// Nearness keys. A format keeps the upper bits of the FP32 word and drops the low
-// kDrop bits (16 for bf16, 13 for fp16 in its normal range); the value is halfway
-// between two neighbours of the format when the dropped bits equal 2^(kDrop-1). The
-// key moves the dropped bits to the top of a word and adds an offset, so that it is
-// at least near_limit<kDrop>() exactly when the dropped bits lie within kSiluUlpBound
-// of the halfway point.
-template <int kDrop>
-constexpr uint32_t near_limit() {
-  return ((1u << kDrop) - 2u * kSiluUlpBound - 1u) << (32 - kDrop);
-}
-template <int kDrop>
-constexpr uint32_t near_offset() {
-  return 0u - (((1u << (kDrop - 1)) + kSiluUlpBound + 1u) << (32 - kDrop));
-}
-template <int kDrop>
-__device__ __forceinline__ uint32_t near_key(float y) {
-  return (__float_as_uint(y) << (32 - kDrop)) + near_offset<kDrop>();
-}
-// The same key in one instruction (the compiler emits a shift and an add, since the
-// fused form takes no literal operand): offset must hold near_offset<kDrop>().
-template <int kDrop>
-__device__ __forceinline__ uint32_t near_key_fused(float y, uint32_t offset) {
-  uint32_t key;
-  asm("v_lshl_add_u32 %0, %1, %2, %3" : "=v"(key) : "v"(y), "n"(32 - kDrop), "s"(offset));
-  return key;
 }
 
 // Dropped bits of each 16-bit format (fp16: normal range; subnormal results are
@@ -142,12 +139,34 @@ constexpr int dropped_bits() {
   return kF == kF16 ? 13 : 16;
 }
 
-// Accumulators at or below this bound take the exact path. Every a with exp2 result
-// at least 2048 (kFastExpLimitBits) lies below about -7.62, so the per-element test
-// flags a superset of what the reduction in activate_rows detects.
-constexpr float kExactBelow = -7.5f;
+// Nearness keys. A format keeps the upper bits of the FP32 word and drops the low
+// dropped_bits<kF>() bits; the value is halfway between two neighbours of the format
+// when they equal half their range. The key moves the dropped bits to the top of a word
+// and adds an offset, so that it is at least near_limit<kF>() exactly when the
+// dropped bits lie within silu_bound<kF>() of the halfway point.
+template <int kF>
+constexpr uint32_t near_limit() {
+  return ((1u << dropped_bits<kF>()) - 2u * silu_bound<kF>() - 1u) << (32 - dropped_bits<kF>());
+}
+template <int kF>
+constexpr uint32_t near_offset() {
+  return 0u - (((1u << (dropped_bits<kF>() - 1)) + silu_bound<kF>() + 1u) << (32 - dropped_bits<kF>()));
+}
+template <int kF>
+__device__ __forceinline__ uint32_t near_key(float y) {
+  return (__float_as_uint(y) << (32 - dropped_bits<kF>())) + near_offset<kF>();
+}
+// The same key in one instruction (the compiler emits a shift and an add, since the
+// fused form takes no literal operand): offset must hold near_offset<kF>().
+template <int kF>
+__device__ __forceinline__ uint32_t near_key_fused(float y, uint32_t offset) {
+  uint32_t key;
+  asm("v_lshl_add_u32 %0, %1, %2, %3" : "=v"(key) : "v"(y), "n"(32 - dropped_bits<kF>()), "s"(offset));
+  return key;
+}
+
 // fp16: a SiLU below 2^-14 in magnitude is an fp16 subnormal, whose rounding
-// boundaries the key does not see. For a above kExactBelow that needs |a| < 2^-12.6
+// boundaries the key does not see. For a above exact_below that needs |a| < 2^-12.6
 // (SiLU(a) = a * sigmoid(a) with sigmoid(a) > 0.4 there), so |a| < 2^-12 goes exact.
 constexpr float kTinyF16 = 0x1p-12f;
 
@@ -265,15 +284,16 @@ __device__ __noinline__ uint32_t act_word_exact(float a, bool silu) {
 // Activation of rows of accumulators.
 
 // Does the word of accumulator a (value y, aux from activate_rows) need the exact
-// path? SiLU, 16-bit formats: y near a rounding boundary, a below kExactBelow, NaN,
-// or (fp16) a subnormal result; SiLU, FP32: the double exp near a binary32 rounding
-// boundary, or a NaN value; identity: NaN.
+// path? SiLU, bf16: y near a rounding boundary (its key recomputed here), a below
+// exact_below, or NaN; SiLU, fp16: the same with the key from aux, or a subnormal
+// result; SiLU, FP32: the double exp near a binary32 rounding boundary (key in aux),
+// or a NaN value; identity: NaN.
 template <int kF, bool kSilu>
 __device__ __forceinline__ bool needs_exact(float a, float y, uint32_t aux) {
   if (!kSilu) return a != a;
   if (kF == kF32) return aux >= kDoubleNearLimit || y != y;
-  constexpr int kDrop = dropped_bits<kF>();
-  const bool near = near_key<kDrop>(y) >= near_limit<kDrop>() || !(a >= kExactBelow);
+  const uint32_t key = kF == kF16 ? aux : near_key<kF>(y);
+  const bool near = key >= near_limit<kF>() || !(a >= exact_below<kF>());
   if (kF == kF16) return near || __builtin_fabsf(a) < kTinyF16;
   return near;
 }
@@ -295,8 +315,7 @@ template <int kF, bool kSilu, int N, int R>
 __device__ __forceinline__ bool activate_rows(const float (&acc)[R][N], float (&y)[R][N],
                                               uint32_t (&aux)[R][N],
                                               uint32_t (&w)[R][row_words<kF, N>()]) {
-  constexpr int kDrop = dropped_bits<kF>();
-  const uint32_t offset = near_offset<kDrop>();
+  const uint32_t offset = near_offset<kF>();
   uint32_t key_max = 0, exp_max = 0;
   float sum = 0.0f;
   float amin = __builtin_inff();
@@ -313,7 +332,9 @@ __device__ __forceinline__ bool activate_rows(const float (&acc)[R][N], float (&
       } else if (kSilu) {
         float e;
         y[r][k] = silu_fast(acc[r][k], e);
-        key_max = max(key_max, near_key_fused<kDrop>(y[r][k], offset));
+        const uint32_t key = near_key_fused<kF>(y[r][k], offset);
+        if (kF == kF16) aux[r][k] = key;
+        key_max = max(key_max, key);
         exp_max = max(exp_max, __float_as_uint(e));
         if (kF == kF16) amin = __builtin_fminf(amin, __builtin_fabsf(acc[r][k]));
       } else {
@@ -334,7 +355,7 @@ __device__ __forceinline__ bool activate_rows(const float (&acc)[R][N], float (&
   }
   if (!kSilu) return sum != sum;
   if (kF == kF32) return key_max >= kDoubleNearLimit || sum != sum;
-  const bool flag = key_max >= near_limit<kDrop>() || exp_max >= kFastExpLimitBits;
+  const bool flag = key_max >= near_limit<kF>() || exp_max >= fast_exp_limit<kF>();
   if (kF == kF16) return flag || amin < kTinyF16;
   return flag;
 }
