@@ -49,6 +49,11 @@ namespace {
 constexpr int kWave = 64;
 constexpr int kGroup = 1;  // rows sharing one rare-path branch (divides R)
 constexpr int kLaneChannels = 4;  // channels per lane
+// Tiles of at most this many rows (short sequences, a sequence's last rows) take a
+// path that loads only kShort rows. On 4096 sequences of 1-4 tokens it measured 15 %
+// faster than loading all R rows; 8 rows gained half as much; longer workloads are
+// unchanged.
+constexpr int kShort = 4;
 constexpr int kMinWaves = 4;  // occupancy target (waves per SIMD)
 // Fixup list entries per wave (8 bytes each in LDS): room for one row group of
 // every lane beyond the entries that trigger a flush.
@@ -238,7 +243,9 @@ struct ConvWorker {
   typedef Lane<V * kBytes> L;
   typedef typename L::vec vec;
   // x rows of a tile as loaded: 3 history rows, then R tile rows.
-  typedef vec Rows[3 + R];
+  template <int RR>
+  using RowsOf = vec[3 + RR];
+  typedef RowsOf<R> Rows;
 
   const ConvParams& P;
   int lane;
@@ -448,22 +455,24 @@ struct ConvWorker {
   // tile's end repeat its last row), so the number of loads never depends on the
   // tile and every load is in bounds. Tile rows are streamed, except the last
   // three, which the next tile of the column block reads again as its history.
-  __device__ __forceinline__ void issue(Rows& buf, const Tile& d) {
+  template <int RR>
+  __device__ __forceinline__ void issue(RowsOf<RR>& buf, const Tile& d) {
     const __amdgpu_buffer_rsrc_t xr =
         make_rsrc(P.x + (int64_t)(d.t0 - d.halo) * P.x_row_stride * kBytes);
 #pragma unroll
     for (int r = 0; r < 3; ++r)
       buf[r] = L::template load<kKeep>(xr, xvo, d.halo ? (uint32_t)r * xrow_bytes : 0u);
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
+    for (int r = 0; r < RR; ++r) {
       const uint32_t off = (uint32_t)(min(r, d.n - 1) + d.halo) * xrow_bytes;
-      buf[3 + r] = r < R - 3 ? L::template load<kStream>(xr, xvo, off)
-                             : L::template load<kKeep>(xr, xvo, off);
+      buf[3 + r] = r < RR - 3 ? L::template load<kStream>(xr, xvo, off)
+                              : L::template load<kKeep>(xr, xvo, off);
     }
   }
 
   // Processes a valid tile whose rows issue() loaded into buf.
-  __device__ __forceinline__ void compute(Rows& buf, const Tile& d) {
+  template <int RR>
+  __device__ __forceinline__ void compute(RowsOf<RR>& buf, const Tile& d) {
     // History e[t0-3], e[t0-2], e[t0-1]: x rows for later tiles; for the first tile
     // of a sequence the stored state if the sequence is live and has an initial
     // state, else zeros.
@@ -547,13 +556,13 @@ struct ConvWorker {
         }
       }
     };
-    if (d.n == R) {
+    if (d.n == RR) {
       // Full tile: straight-line code, no conditions.
 #pragma unroll
-      for (int r0 = 0; r0 < R; r0 += kGroup) group(r0, kGroup);
+      for (int r0 = 0; r0 < RR; r0 += kGroup) group(r0, kGroup);
     } else {
 #pragma unroll
-      for (int r0 = 0; r0 < R; r0 += kGroup)
+      for (int r0 = 0; r0 < RR; r0 += kGroup)
         if (r0 < d.n) group(r0, min(kGroup, d.n - r0));
     }
 
@@ -606,9 +615,18 @@ __global__ __launch_bounds__(kWave * kG) __attribute__((amdgpu_waves_per_eu(kMin
   w.load_weights();
   const Tile d = describe_tile<R>(P, p, lane);
   if (!d.valid) return;
-  typename ConvWorker<kF, V, R, kBias, kSilu>::Rows buf;
-  w.issue(buf, d);
-  w.compute(buf, d);
+  typedef ConvWorker<kF, V, R, kBias, kSilu> W;
+  if (kShort > 0 && d.n <= kShort) {
+    // A tile of at most kShort rows (short sequences, or a sequence's last rows):
+    // only those rows are loaded.
+    typename W::template RowsOf<kShort> buf;
+    w.template issue<kShort>(buf, d);
+    w.template compute<kShort>(buf, d);
+  } else {
+    typename W::Rows buf;
+    w.template issue<R>(buf, d);
+    w.template compute<R>(buf, d);
+  }
   w.finish();
 }
 
