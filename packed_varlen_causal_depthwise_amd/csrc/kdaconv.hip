@@ -9,13 +9,13 @@
 // kLaneChannels consecutive channels, so every x row and every output row of the
 // tile moves as one vector per lane (8 bytes for bf16 and fp16, 16 for FP32; R is
 // 16 for the 16-bit formats and 8 for FP32, so a wave's loads in flight stay the
-// same). Programs are numbered so that sequence s owns programs v(s) .. v(s+1)-1
-// with v(s) = s + floor(qsl[s] / R); the wave
-// finds its sequence on the device with a radix-64 search over query_start_loc
-// (one ballot per level), so the grid, cdiv(T, R) + num_seqs programs times
-// the column blocks, depends only on host sizes and the launch can be captured in
-// a graph. Tile j of sequence s covers rows [start + j*R, start + (j+1)*R)
-// of the sequence; programs past the end of their sequence exit at once. The
+// same). Tile j of sequence s covers rows [start + j*R, start + (j+1)*R) of the
+// sequence. Programs 0 .. num_seqs-1 are the sequences' first tiles, which need no
+// search; program num_seqs + q is the later tile (if any) starting in rows
+// [(q+1) R, (q+2) R), whose sequence the wave finds with a radix-64 search over
+// query_start_loc (one ballot per level). The grid, num_seqs + cdiv(T, R) programs
+// times the column blocks, depends only on host sizes, so the launch can be
+// captured in a graph; programs without a tile exit at once. The
 // launch is one-dimensional with the column block varying fastest, so waves
 // dispatched together cover whole rows; waves are short, and the dispatcher keeps
 // every SIMD supplied with new ones until the end (long-lived waves started
@@ -162,25 +162,24 @@ __device__ __forceinline__ void unpack(typename Lane<V * element_bytes<kF>()>::v
   }
 }
 
-// Sequence s of program p and its raw bounds qsl[s], qsl[s + 1]; s = -1 if none.
+// Sequence s and its raw bounds qsl[s], qsl[s + 1]; s = -1 if none.
 struct SeqBounds {
   int s;
   int q0;
   int q1;
 };
 
-// Largest s in [0, num_seqs) with s + floor(qsl[s] / R) <= p, with qsl[s] and
-// qsl[s + 1]. v(s) is strictly increasing for a non-decreasing qsl, so at each level
-// the lanes whose candidate passes form a prefix of the wave. The last level reads
-// consecutive entries, so the bounds are taken from its lanes rather than loaded
-// again: a wave's loads of x wait on one round trip to qsl per level.
-template <int R>
-__device__ __forceinline__ SeqBounds find_sequence(const ConvParams& P, int p, int lane) {
+// The sequence containing row r: the largest s in [0, num_seqs) with qsl[s] <= r,
+// with qsl[s] and qsl[s + 1], by a radix-64 search (one ballot per level; for a
+// non-decreasing qsl the lanes whose entry passes form a prefix of the wave). The
+// last level reads consecutive entries, so the bounds come from its lanes: a wave
+// waits on one round trip to qsl per level.
+__device__ __forceinline__ SeqBounds find_sequence(const ConvParams& P, int r, int lane) {
   if (P.search_levels == 0) {
     // One sequence: both bounds in one round trip.
     const int q0 = P.qsl[0];
     const int q1 = P.qsl[1];
-    if (max(q0, 0) / R > p) return SeqBounds{-1, 0, 0};
+    if (q0 > r) return SeqBounds{-1, 0, 0};
     return SeqBounds{0, q0, q1};
   }
   int base = 0;
@@ -190,7 +189,7 @@ __device__ __forceinline__ SeqBounds find_sequence(const ConvParams& P, int p, i
   for (int level = 0; level < P.search_levels; ++level) {
     const int idx = base + lane * stride;
     q = idx <= P.num_seqs ? P.qsl[idx] : 0;  // qsl has num_seqs + 1 entries
-    const bool ok = idx < P.num_seqs && idx + max(q, 0) / R <= p;
+    const bool ok = idx < P.num_seqs && q <= r;
     const uint64_t m = __ballot(ok);
     cnt = __popcll(m);
     if (cnt == 0) return SeqBounds{-1, 0, 0};
@@ -214,22 +213,45 @@ struct Tile {
   int end;  // one past the sequence's last row
 };
 
+// Program map. Programs [0, num_seqs) are the first tiles of the sequences, in
+// order: no search, and the sequence's line and state can be requested at once.
+// Program num_seqs + q takes the later tile (j >= 1) whose first row lies in
+// [(q + 1) R, (q + 2) R), if there is one. Every later tile is preceded by R rows of
+// its own sequence, so later tiles start at least R rows apart and each block holds
+// at most one; its sequence is the one containing row (q + 1) R. With q below
+// cdiv(T, R) every later tile has a program, and the grid, num_seqs + cdiv(T, R)
+// programs per column block, depends only on host sizes.
 template <int R>
 __device__ __forceinline__ Tile describe_tile(const ConvParams& P, int p, int lane) {
   Tile d{0, 0, 0, 0, 1, 0, 0};
-  const SeqBounds b = find_sequence<R>(P, p, lane);
-  if (b.s < 0) return d;
   const int T = P.num_tokens;
+  if (p < P.num_seqs) {
+    const int start = min(max(P.qsl[p], 0), T);
+    const int end = min(max(P.qsl[p + 1], start), T);
+    if (end <= start) return d;  // empty sequence
+    d.valid = 1;
+    d.s = p;
+    d.t0 = start;
+    d.n = min(R, end - start);
+    d.end = end;
+    return d;
+  }
+  const int r0 = (p - P.num_seqs + 1) * R;
+  if (r0 >= T) return d;
+  const SeqBounds b = find_sequence(P, r0, lane);
+  if (b.s < 0) return d;
   const int start = min(max(b.q0, 0), T);
   const int end = min(max(b.q1, start), T);
-  const int j = p - (b.s + start / R);
-  if ((int64_t)j * R >= end - start) return d;  // past the end of its sequence
+  if (r0 < start || r0 >= end) return d;
+  const int j = (r0 - start + R - 1) / R;  // the first tile starting at or after r0
+  const int t0 = start + j * R;
+  if (j < 1 || t0 >= end) return d;
   d.valid = 1;
   d.s = b.s;
   d.j = j;
-  d.t0 = start + j * R;
-  d.n = min(R, end - d.t0);
-  d.halo = j > 0 ? 3 : 0;
+  d.t0 = t0;
+  d.n = min(R, end - t0);
+  d.halo = 3;
   d.end = end;
   return d;
 }
