@@ -327,7 +327,7 @@ def main() -> int:
         # Decode steps (one token per sequence) on the same channels.
         result["decode"] = {
             str(bsz): time_decode(kd, torch, workloads.decode_batch(bsz), steps=100, warmup=10)
-            for bsz in (64, 256, 1024)
+            for bsz in (64, 256, 1024, 4096)
         }
         # The same 16K-token workload with fp16 and FP32 x (output in x's format).
         result["other_formats"] = {

@@ -30,9 +30,12 @@ def _run_update(x_words, fmt, dim, weight, bias, states_dev, ci, pd, act, null):
 
 
 @pytest.mark.parametrize("fmt", ["bf16", "f16", "f32"])
+# Waves take 1, 2, 4 or 8 sequences depending on the batch (at least 2048 waves per
+# launch); the batches below cover each, with a last wave that is only partly used.
 @pytest.mark.parametrize("batch,parts,pd,act", [(1, 3, 256, "silu"), (7, 3, 200, None),
                                                 (64, 3, 1536, "silu"), (300, 3, 192, "silu"),
-                                                (4096, 3, 192, None)])
+                                                (4096, 3, 192, None), (4093, 3, 192, "silu"),
+                                                (250, 3, 1536, "silu"), (1021, 3, 1536, "silu")])
 def test_decode_step_bit_exact(batch, parts, pd, act, fmt):
     dim = parts * pd
     lines = batch + 5

@@ -252,11 +252,12 @@ def config5(seed: int = 5, x_dtype: str = "bf16") -> Workload:
 
 def decode_batch(batch: int = 256, seed: int = 6, x_dtype: str = "bf16") -> Workload:
     """A decode step: ``batch`` sequences of one token each, dim 4608 (3 x 1536) in rows
-    of 9728, every sequence continuing from its stored line (1024 lines), bias, SiLU.
+    of 9728, every sequence continuing from its own stored line (max(1024, batch)
+    lines), bias, SiLU.
     As a Workload its offsets are 0, 1, ..., batch and every initial-state flag is set,
     which is what the decode entry point computes."""
     rng = np.random.Generator(np.random.PCG64(seed))
-    dim, lines = 4608, 1024
+    dim, lines = 4608, max(1024, batch)  # one distinct line per sequence
     x = _x_buffer(rng, batch, dim, IN_PROJ_ROW_STRIDE, x_dtype=x_dtype)
     w = _normal(rng, (dim, 4), 0.5)
     b = _normal(rng, (dim,), 0.1)
