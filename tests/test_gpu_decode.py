@@ -110,3 +110,41 @@ def test_decode_bench_workload(fmt):
     want, want_st = oracle.run_workload(wl)
     assert np.array_equal(got, want), first_mismatches(got, want)
     assert np.array_equal(st_dev.cpu().numpy().view(np.uint32), want_st.view(np.uint32))
+
+
+def test_decode_graph_replay_with_new_device_data():
+    """One decode step captured in a HIP graph and replayed on new x, lines and line
+    choices of the same shapes: every replay matches the oracle for its data."""
+    B, dim, pd = 96, 768, 256
+    base = make_workload([1] * B, dim=dim, part_dim=pd, seed=95, lines=B + 8)
+    x = words_to_torch(base.x, torch.bfloat16)[:, :dim].contiguous()
+    w = torch.from_numpy(base.weight).cuda()
+    b = torch.from_numpy(base.bias).cuda()
+    st = torch.from_numpy(base.conv_states.copy()).cuda()
+    ci = torch.from_numpy(base.cache_indices).cuda()
+    out = torch.empty((3, B, pd), dtype=torch.bfloat16, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        kd.packed_causal_conv1d_update(x, w, b, st, ci, pd, "silu", None, out=out)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        kd.packed_causal_conv1d_update(x, w, b, st, ci, pd, "silu", None, out=out)
+    for trial in range(3):
+        wl = make_workload([1] * B, dim=dim, part_dim=pd, seed=96 + trial, lines=B + 8)
+        x.copy_(words_to_torch(wl.x, torch.bfloat16)[:, :dim])
+        w.copy_(torch.from_numpy(wl.weight))
+        b.copy_(torch.from_numpy(wl.bias))
+        st.copy_(torch.from_numpy(wl.conv_states))
+        ci.copy_(torch.from_numpy(wl.cache_indices))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        want_st = wl.conv_states.copy()
+        want = oracle.packed_causal_conv1d_update(wl.x, dim, wl.weight, wl.bias, want_st,
+                                                  wl.cache_indices, pd, "silu", None)
+        got = torch_to_words(out)
+        assert np.array_equal(got, want), (trial, first_mismatches(got, want))
+        assert np.array_equal(st.cpu().numpy().view(np.uint32), want_st.view(np.uint32)), trial
