@@ -128,7 +128,7 @@ struct ConvParams {
   int32_t col_begin;  // first channel of this launch
   int32_t col_end;  // one past its last channel
   int32_t col_blocks;  // column blocks of 64 * kLaneChannels channels in this launch
-  int32_t programs;  // cdiv(num_tokens, R) + num_seqs
+  int32_t programs;  // programs per column block
   int32_t part_dim;
   int32_t search_levels;  // radix-64 levels: smallest L with 64^L >= num_seqs
   int32_t search_top;  // 64^(search_levels - 1)
@@ -256,9 +256,9 @@ __device__ __forceinline__ Tile describe_tile(const ConvParams& P, int p, int la
   return d;
 }
 
-// The per-wave part of the convolution shared by both kernels: the lane's
-// channels, its weights and bias, and the processing of one tile whose x rows
-// were loaded by issue().
+// The per-wave part of the convolution shared by the prefill and decode kernels:
+// the lane's channels, its weights and bias, the state line's I/O, the processing
+// of one prefill tile whose x rows were loaded by issue(), and decode steps.
 template <int kF, int V, int R, bool kBias, bool kSilu>
 struct ConvWorker {
   static constexpr int kBytes = element_bytes<kF>();
