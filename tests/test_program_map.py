@@ -1,29 +1,57 @@
 """The prefill kernel's program map, checked as arithmetic on the CPU.
 
-Programs [0, S) are the first tiles of the sequences; program S + q is the later
-tile (tile index j >= 1) whose first row lies in [(q + 1) R, (q + 2) R), found
-through the sequence that contains row (q + 1) R. The kernel's describe_tile
-evaluates the same formulas; these tests check that the map, over a grid of
-S + cdiv(T, R) programs, names every tile of every sequence exactly once
-(empty sequences, padding rows, every tile size the kernel uses). The GPU parity
-tests check the kernel itself.
+Programs [0, S) are the first tiles of the sequences. The later programs go to row
+blocks q: block q owns the later tile (tile index j >= 1) whose first row lies in
+[(q + 1) R, (q + 2) R), found through the sequence that contains row (q + 1) R.
+Blocks below split_half take one program each, blocks in [split_half,
+split_quarter) two (one half of the tile's rows each) and the rest four (one
+quarter each); the host picks the split points so that a fixed number of waves
+compute half and quarter tiles at the end of the launch. The kernel's
+describe_tile and launch evaluate the same formulas; these tests check that the
+map, over the grid the host launches, computes every row of every sequence exactly
+once, with the 3 rows before each later part inside the same sequence (empty
+sequences, padding rows, every tile size and column-block count the kernel uses).
+The GPU parity tests check the kernel itself.
 """
 
 import numpy as np
 import pytest
 
+HALF_TILE_WAVES = 2304
+QUARTER_TILE_WAVES = 1152
 
-def _tiles_by_map(qsl, T, R):
+
+def _split(T, R, col_blocks):
+    blocks = max(0, -(-T // R) - 1)
+    quarter = min(blocks, -(-QUARTER_TILE_WAVES // (4 * col_blocks)))
+    half = min(blocks - quarter, -(-HALF_TILE_WAVES // (2 * col_blocks)))
+    return blocks - quarter - half, blocks - quarter, half, quarter
+
+
+def _parts_by_map(qsl, T, R, col_blocks):
+    """(sequence, first row, rows, halo) for every program that has work."""
     S = len(qsl) - 1
+    split_half, split_quarter, half, quarter = _split(T, R, col_blocks)
+    programs = S + split_half + 2 * half + 4 * quarter
     got = []
-    for p in range(S + (T + R - 1) // R):
+    for p in range(programs):
         if p < S:
             start = min(max(qsl[p], 0), T)
             end = min(max(qsl[p + 1], start), T)
             if end > start:
-                got.append((p, 0))
+                got.append((p, start, min(R, end - start), 0))
             continue
-        r0 = (p - S + 1) * R
+        pl = p - S
+        if pl < split_half:
+            q, parts, h = pl, 1, 0
+        else:
+            ph = pl - split_half
+            nh = 2 * (split_quarter - split_half)
+            if ph < nh:
+                q, parts, h = split_half + ph // 2, 2, ph % 2
+            else:
+                q, parts, h = split_quarter + (ph - nh) // 4, 4, (ph - nh) % 4
+        r0 = (q + 1) * R
         if r0 >= T:
             continue
         cand = [s for s in range(S) if qsl[s] <= r0]
@@ -38,28 +66,54 @@ def _tiles_by_map(qsl, T, R):
         t0 = start + j * R
         if j < 1 or t0 >= end:
             continue
-        got.append((s, j))
+        ts = t0 + h * (R // parts)
+        n = min(R // parts, min(t0 + R, end) - ts)
+        if n <= 0:
+            continue
+        got.append((s, ts, n, 3))
     return got
 
 
-@pytest.mark.parametrize("R", [4, 8, 16])
-def test_every_tile_exactly_once(R):
-    rng = np.random.default_rng(R)
-    for _ in range(600):
+def _check_cover(qsl, T, R, col_blocks):
+    S = len(qsl) - 1
+    got = _parts_by_map(qsl, T, R, col_blocks)
+    seen = np.zeros(T, dtype=int)
+    for s, ts, n, halo in got:
+        start, end = qsl[s], qsl[s + 1]
+        assert start <= ts and ts + n <= end
+        assert ts - halo >= start  # history rows belong to the sequence
+        assert halo == 0 or ts - start >= R  # later parts never touch the state
+        seen[ts:ts + n] += 1
+    want = np.zeros(T, dtype=int)
+    for s in range(S):
+        want[qsl[s]:qsl[s + 1]] = 1
+    assert np.array_equal(seen, want)
+    firsts = [g for g in got if g[3] == 0]
+    assert sorted(g[0] for g in firsts) == [s for s in range(S) if qsl[s + 1] > qsl[s]]
+
+
+@pytest.mark.parametrize("R", [8, 16])
+@pytest.mark.parametrize("col_blocks", [1, 3, 18, 200])
+def test_every_row_exactly_once(R, col_blocks):
+    rng = np.random.default_rng(R * 1000 + col_blocks)
+    for _ in range(300):
         S = int(rng.integers(1, 40))
-        lens = rng.integers(0, 60, size=S)
+        lens = rng.integers(0, 60 if _ % 2 else 400, size=S)
         lens[rng.random(S) < 0.3] = 0
         qsl = np.concatenate([[0], np.cumsum(lens)]).astype(int)
         T = int(qsl[-1]) + int(rng.integers(0, 20))
         if T == 0:
             continue
-        want = sorted((s, j) for s in range(S) for j in range(-(-int(lens[s]) // R)))
-        got = _tiles_by_map(qsl, T, R)
-        assert len(got) == len(set(got))
-        assert sorted(got) == want
+        _check_cover(qsl, T, R, col_blocks)
 
 
 def test_one_long_sequence():
+    """16384 tokens over 18 column blocks: 943 whole tiles, 64 tiles in halves and 16
+    in quarters after the first tile, i.e. the last 1024 rows in 8-row parts and the
+    256 before the end in 4-row parts."""
     qsl = np.array([0, 16384])
-    got = _tiles_by_map(qsl, 16384, 16)
-    assert got == [(0, j) for j in range(1024)]
+    got = _parts_by_map(qsl, 16384, 16, 18)
+    assert got[0] == (0, 0, 16, 0)
+    sizes = [n for _, _, n, _ in got[1:]]
+    assert sizes == [16] * 943 + [8] * 128 + [4] * 64
+    _check_cover(qsl, 16384, 16, 18)
