@@ -139,6 +139,10 @@ struct ConvParams {
   int32_t programs;  // programs per column block
   int32_t split_half;  // first row block whose later tile is taken by 2 programs
   int32_t split_quarter;  // first row block whose later tile is taken by 4 programs
+  // Division of the workgroup index by the workgroups per program (set by the
+  // launcher): n / groups = (umulhi(n, group_magic) + n) >> group_shift for n < 2^31.
+  uint32_t group_magic;
+  int32_t group_shift;
   int32_t part_dim;
   int32_t search_levels;  // radix-64 levels: smallest L with 64^L >= num_seqs
   int32_t search_top;  // 64^(search_levels - 1)
@@ -149,6 +153,32 @@ struct ConvParams {
   int32_t state_rows;  // each state line is 3 rows of dim contiguous channels ("dim first"),
                        // 16-byte aligned, row and line strides multiples of 4
 };
+
+// Program and column block of this wave: the workgroup index divided by the
+// workgroups per program, by multiplication (the hardware has no integer divide,
+// and a division by a run-time value would put a dependent chain of about thirty
+// instructions in front of every wave's first load).
+struct WaveSlot {
+  int p;
+  int cb;
+};
+template <int kG>
+__device__ __forceinline__ WaveSlot wave_slot(const ConvParams& P, int wave) {
+  const uint32_t n = blockIdx.x;
+  const uint32_t p = (__umulhi(n, P.group_magic) + n) >> P.group_shift;
+  const uint32_t groups = ((uint32_t)P.col_blocks + kG - 1) / kG;
+  return WaveSlot{(int)p, (int)(n - p * groups) * kG + wave};
+}
+
+// The multiplier and shift of wave_slot for a divisor d >= 1: l = ceil(log2 d),
+// m = floor(2^32 (2^l - d) / d) + 1 (the round-up method of Granlund and
+// Montgomery); exact for every n < 2^31.
+void set_group_division(ConvParams& P, uint64_t d) {
+  int l = 0;
+  while ((1ull << l) < d) ++l;
+  P.group_magic = (uint32_t)(((1ull << 32) * ((1ull << l) - d)) / d + 1);
+  P.group_shift = l;
+}
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, kRange, kDescWord3);
@@ -690,9 +720,9 @@ __global__ __launch_bounds__(kWave * kG) __attribute__((amdgpu_waves_per_eu(kMin
   static_assert(V % 4 == 0, "the vector weight, bias and state paths take 4 channels at a time");
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
-  const uint32_t groups = ((uint32_t)P.col_blocks + kG - 1) / kG;  // workgroups per program
-  const int p = (int)(blockIdx.x / groups);
-  const int cb = (int)(blockIdx.x - (uint32_t)p * groups) * kG + wave;
+  const WaveSlot slot = wave_slot<kG>(P, wave);
+  const int p = slot.p;
+  const int cb = slot.cb;
   if (cb >= P.col_blocks) return;
   // Weights first: their loads overlap the search for the tile's sequence.
   __shared__ uint2 fix_slots[kG][kFixCapacity];
@@ -727,9 +757,9 @@ template <int kF, int V, int kSeq, int kG, bool kBias, bool kSilu>
 __global__ __launch_bounds__(kWave * kG) void packed_conv_update_kernel(const ConvParams P) {
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
-  const uint32_t groups = ((uint32_t)P.col_blocks + kG - 1) / kG;
-  const int p = (int)(blockIdx.x / groups);
-  const int cb = (int)(blockIdx.x - (uint32_t)p * groups) * kG + wave;
+  const WaveSlot slot = wave_slot<kG>(P, wave);
+  const int p = slot.p;
+  const int cb = slot.cb;
   if (cb >= P.col_blocks) return;
   ConvWorker<kF, V, 1, kBias, kSilu> w(P, lane, cb, nullptr);
   w.load_weights();
@@ -820,9 +850,10 @@ int validate(const void* x, int dtype, int64_t num_tokens, int64_t dim, int64_t 
 }
 
 template <int kF, int V, int kG>
-void launch_group(const ConvParams& P, bool bias, bool silu, hipStream_t st) {
+void launch_group(ConvParams P, bool bias, bool silu, hipStream_t st) {
   constexpr int R = rows_per_tile<kF>();
   const uint64_t groups = ((uint64_t)P.col_blocks + kG - 1) / kG;
+  set_group_division(P, groups);
   const dim3 grid((unsigned)((uint64_t)P.programs * groups));
   const dim3 block(kWave * kG);
   if (bias) {
@@ -859,8 +890,9 @@ void launch(ConvParams P, int64_t cols, bool bias, bool silu, hipStream_t st) {
 }
 
 template <int kF, int V, int kSeq, int kG>
-void launch_update_group(const ConvParams& P, bool bias, bool silu, hipStream_t st) {
+void launch_update_group(ConvParams P, bool bias, bool silu, hipStream_t st) {
   const uint64_t groups = ((uint64_t)P.col_blocks + kG - 1) / kG;
+  set_group_division(P, groups);
   const dim3 grid((unsigned)((uint64_t)P.programs * groups));
   const dim3 block(kWave * kG);
   if (bias) {
@@ -931,6 +963,8 @@ void fill_common(ConvParams& P, const void* x, int64_t num_tokens, int64_t x_row
   P.search_top = 1;
   P.split_half = 0;
   P.split_quarter = 0;
+  P.group_magic = 1;
+  P.group_shift = 0;
   P.has_null_block = has_null_block != 0;
   P.weight_vec = ws0 == 4 && ws1 == 1 && aligned16(weight);
   P.bias_vec = bias != nullptr && aligned16(bias);

@@ -117,3 +117,19 @@ def test_one_long_sequence():
     sizes = [n for _, _, n, _ in got[1:]]
     assert sizes == [16] * 943 + [8] * 128 + [4] * 64
     _check_cover(qsl, 16384, 16, 18)
+
+
+def test_workgroup_division_by_multiplication():
+    """The launcher's multiplier and shift (l = ceil(log2 d), m = floor(2^32 (2^l - d)/d)
+    + 1) divide every workgroup index below 2^31 exactly, for every divisor up to 2^22
+    that a launch can have (sampled)."""
+    rng = np.random.default_rng(5)
+    divisors = list(range(1, 1100)) + [int(v) for v in rng.integers(1, 1 << 22, size=400)]
+    for d in divisors:
+        l = (d - 1).bit_length()
+        m = ((1 << 32) * ((1 << l) - d)) // d + 1
+        assert 0 < m < (1 << 32)
+        ns = np.concatenate([[0, 1, d - 1, d, d + 1, (1 << 31) - 1],
+                             rng.integers(0, 1 << 31, size=300)]).astype(object)
+        for n in ns:
+            assert ((((n * m) >> 32) + n) >> l) == n // d
