@@ -6,7 +6,8 @@ blocks q: block q owns the later tile (tile index j >= 1) whose first row lies i
 Blocks below split_half take one program each, blocks in [split_half,
 split_quarter) two (one half of the tile's rows each) and the rest four (one
 quarter each); the host picks the split points so that a fixed number of waves
-compute half and quarter tiles at the end of the launch. The kernel's
+compute half and quarter tiles at the end of the launch, and splits nothing when
+the sequences average under two tiles. The kernel's
 describe_tile and launch evaluate the same formulas; these tests check that the
 map, over the grid the host launches, computes every row of every sequence exactly
 once, with the 3 rows before each later part inside the same sequence (empty
@@ -21,17 +22,18 @@ HALF_TILE_WAVES = 2304
 QUARTER_TILE_WAVES = 1152
 
 
-def _split(T, R, col_blocks):
+def _split(T, S, R, col_blocks):
     blocks = max(0, -(-T // R) - 1)
-    quarter = min(blocks, -(-QUARTER_TILE_WAVES // (4 * col_blocks)))
-    half = min(blocks - quarter, -(-HALF_TILE_WAVES // (2 * col_blocks)))
+    split = T >= 2 * R * S
+    quarter = min(blocks, -(-QUARTER_TILE_WAVES // (4 * col_blocks))) if split else 0
+    half = min(blocks - quarter, -(-HALF_TILE_WAVES // (2 * col_blocks))) if split else 0
     return blocks - quarter - half, blocks - quarter, half, quarter
 
 
 def _parts_by_map(qsl, T, R, col_blocks):
     """(sequence, first row, rows, halo) for every program that has work."""
     S = len(qsl) - 1
-    split_half, split_quarter, half, quarter = _split(T, R, col_blocks)
+    split_half, split_quarter, half, quarter = _split(T, S, R, col_blocks)
     programs = S + split_half + 2 * half + 4 * quarter
     got = []
     for p in range(programs):
@@ -133,3 +135,58 @@ def test_workgroup_division_by_multiplication():
                              rng.integers(0, 1 << 31, size=300)]).astype(object)
         for n in ns:
             assert ((((n * m) >> 32) + n) >> l) == n // d
+
+
+def _division(d):
+    l = (d - 1).bit_length()
+    return ((1 << 32) * ((1 << l) - d)) // d + 1, l
+
+
+def _wave_slot(n, groups, programs, xcd_chunks):
+    """(program, column group) of workgroup n, as the kernels' wave_slot computes it."""
+    gm, gl = _division(groups)
+    cm, cl = _division(8 * groups)
+    full = programs // 8 if xcd_chunks else 0
+    c = (((n * cm) >> 32) + n) >> cl
+    if c < full:
+        k = n - c * 8 * groups
+        x, i, whole = k & 7, k >> 3, groups >> 3
+        if i < 8 * whole:
+            g, pi = 8 * (i >> 3) + x, i & 7
+        else:
+            L = x * (groups & 7) + (i - 8 * whole)
+            g, pi = 8 * whole + (L >> 3), L & 7
+        return 8 * c + pi, g
+    b = n - full * 8 * groups
+    p = (((b * gm) >> 32) + b) >> gl
+    return 8 * full + p, b - p * groups
+
+
+@pytest.mark.parametrize("xcd_chunks", [False, True])
+def test_workgroup_order_is_a_bijection(xcd_chunks):
+    for groups in [1, 2, 3, 5, 7, 8, 9, 12, 16, 17, 40]:
+        for programs in [1, 7, 8, 9, 23, 64, 200]:
+            seen = set()
+            for n in range(programs * groups):
+                p, g = _wave_slot(n, groups, programs, xcd_chunks)
+                assert 0 <= p < programs and 0 <= g < groups
+                seen.add((p, g))
+            assert len(seen) == programs * groups
+
+
+def test_prefill_order_keeps_column_groups_on_one_xcd():
+    """16384 tokens x 4608 channels: 9 column groups of 2 waves; the tile below a tile
+    in the same column group runs on the same XCD (workgroup index mod 8) for 8 of
+    every 9 groups, and the rows are still visited chunk by chunk in order."""
+    groups, programs = 9, 1 + 943 + 128 + 64
+    xcd = {}
+    order = []
+    for n in range(programs * groups):
+        p, g = _wave_slot(n, groups, programs, True)
+        xcd[(p, g)] = n % 8
+        order.append(p)
+    pairs = [(p, g) for (p, g) in xcd if (p + 1, g) in xcd]
+    local = sum(xcd[(p, g)] == xcd[(p + 1, g)] for p, g in pairs)
+    assert local / len(pairs) > 0.88
+    # Every workgroup of chunk c is dispatched before any of chunk c + 1.
+    assert all(order[n] // 8 <= order[m] // 8 for n, m in zip(range(len(order) - 1), range(1, len(order))))
