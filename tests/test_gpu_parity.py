@@ -61,6 +61,19 @@ def test_many_sequences_three_search_levels():
     _compare(wl)
 
 
+@pytest.mark.parametrize("dim,part_dim", [(2304, 768), (4096, 1024), (6656, 1664), (8704, 4352)])
+def test_xcd_chunk_order_and_split_tail(dim, part_dim):
+    """Launches with at least 8 column groups take the XCD-chunked workgroup order; these
+    dims give 9 groups of one wave, and 8, 13 and 17 groups of two waves (no remainder,
+    remainders of 5 and 1), with a partial last chunk of programs and the launch's last
+    row blocks split into half and quarter tiles. Padding rows follow the sequences."""
+    from helpers import make_workload
+
+    wl = make_workload([1500, 17, 250, 3], dim=dim, part_dim=part_dim, seed=dim, row_stride=dim + 64,
+                       init=[True, False, True, True], pad_tokens=5)
+    _compare(wl)
+
+
 def test_dim_not_a_multiple_of_the_wave_width():
     from helpers import make_workload
 
