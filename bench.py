@@ -43,9 +43,14 @@ COUNTERS = ROOT / "profiles" / "packed_conv_kernel_16k_tokens_counters.md"
 
 
 def kernel_source_hash() -> str:
+    """Hash of the kernel sources with // comments and blank lines removed, so that a
+    counter summary stays valid across comment-only edits."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        h.update(p.read_bytes())
+        for line in p.read_text().splitlines():
+            code = line.split("//", 1)[0].rstrip()
+            if code:
+                h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

@@ -11,20 +11,23 @@
 // 16 for the 16-bit formats and 8 for FP32, so a wave's loads in flight stay the
 // same). Tile j of sequence s covers rows [start + j*R, start + (j+1)*R) of the
 // sequence. Programs 0 .. num_seqs-1 are the sequences' first tiles, which need no
-// search; program num_seqs + q is the later tile (if any) starting in rows
-// [(q+1) R, (q+2) R), whose sequence the wave finds with a radix-64 search over
-// query_start_loc (one ballot per level). The grid, num_seqs + cdiv(T, R) programs
-// times the column blocks, depends only on host sizes, so the launch can be
-// captured in a graph; programs without a tile exit at once. The
-// launch is one-dimensional with the column block varying fastest, so waves
-// dispatched together cover whole rows; waves are short, and the dispatcher keeps
-// every SIMD supplied with new ones until the end (long-lived waves started
-// together finish unevenly, since a SIMD issues from its oldest wave first).
+// search; the later programs go to row blocks q, each owning the later tile (if
+// any) that starts in rows [(q+1) R, (q+2) R), whose sequence the wave finds with a
+// radix-64 search over query_start_loc (one ballot per level). The last row blocks
+// are split into halves and quarters (describe_tile), so that the waves that run at
+// the end of the launch are short. The grid depends only on host sizes, so the
+// launch can be captured in a graph; programs without a tile exit at once. The
+// launch is one-dimensional; workgroups dispatched together cover whole rows, in
+// chunks ordered so that each column group stays on one XCD (wave_slot). Waves are
+// short, and the dispatcher keeps every SIMD supplied with new ones until the end
+// (long-lived waves started together finish unevenly, since a SIMD issues from its
+// oldest wave first).
 //
 // Memory. A wave issues the loads of its 3 history rows and of all its tile rows
 // before any arithmetic. Tile rows are streamed (nontemporal), except the last
 // three, which the next tile of the column block reads again as its history and
-// which therefore stay cacheable, like the history loads themselves. Outputs are
+// which therefore stay cacheable (in the L2 of the XCD that runs both tiles), like
+// the history loads themselves. Outputs are
 // streamed. x and out are addressed through buffer descriptors based at the
 // tile's first row: the lane's channel offset is a fixed vector register and each
 // row's offset a scalar. Lanes past the launch's last channel (only in a partial
@@ -761,9 +764,10 @@ struct ConvWorker {
   }
 };
 
-// One wave per tile; a workgroup holds kG waves, the same rows in kG adjacent
-// column blocks. The launch is one-dimensional with the column block varying
-// fastest, so workgroups dispatched together cover whole rows.
+// One wave per tile (or part of one); a workgroup holds kG waves, the same rows in
+// kG adjacent column blocks (a column group). wave_slot maps the one-dimensional
+// launch to programs and column groups so that workgroups dispatched together cover
+// whole rows.
 template <int kF, int V, int R, int kG, bool kBias, bool kSilu>
 __global__ __launch_bounds__(kWave * kG) __attribute__((amdgpu_waves_per_eu(kMinWaves))) void packed_conv_kernel(const ConvParams P) {
   static_assert(V % 4 == 0, "the vector weight, bias and state paths take 4 channels at a time");
