@@ -17,12 +17,17 @@ channel), metadata (workloads.Workload.algorithmic_bytes).
 
 cpu_baseline: the CPU oracle as it stands (single thread) on the same workload.
 
+Beside the headline (parity cases and context, not the metric): per-launch times
+of the four other named workloads, decode batches, fp16 and FP32 x, and one
+sequence of 2K, 4K and 8K tokens.
+
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
 """
 
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -179,6 +184,23 @@ def time_decode(kd, torch, wl, steps: int, warmup: int, sets: int = 4):
     }
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def device_info(torch, dev) -> dict:
+    props = torch.cuda.get_device_properties(dev)
+    return {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
+            "compute_units": props.multi_processor_count,
+            "memory_gib": round(props.total_memory / 2**30, 1)}
+
+
 def cpu_baseline(wl, runs: int):
     import oracle
 
@@ -192,6 +214,8 @@ def cpu_baseline(wl, runs: int):
         "value": round(wl.algorithmic_bytes() / med / 1e9, 4),
         "unit": "GB/s",
         "cores": 1,
+        "cpu_model": cpu_model(),
+        "host_cpus": len(os.sched_getaffinity(0)),
         "kind": "oracle",
         "sample": f"the whole workload ({wl.num_tokens} tokens x {wl.dim} channels), "
                   f"{runs} runs, median {med:.2f} s per run, single thread",
@@ -300,6 +324,7 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
+        "device": device_info(torch, dev),
         "config": {
             "workload": "packed varlen causal depthwise conv: 1 sequence x 16384 tokens, "
                         "dim 4608 = 3 x 1536 (x row stride 9728), FP32 weight + bias, SiLU, "
@@ -339,6 +364,16 @@ def main() -> int:
             fmt: time_config(kd, torch, workloads.config3(x_dtype=fmt), steps=100, warmup=10)
             for fmt in ("f16", "f32")
         }
+        # Context: one sequence of 2K-16K tokens (the first rows of the headline workload),
+        # enough buffer sets rotated that they exceed the Infinity Cache.
+        result["context_sweep"] = {}
+        for tokens in (2048, 4096, 8192):
+            sub = dataclasses.replace(wl, name=f"1 x {tokens} tokens, dim 4608, stride 9728",
+                                      x=wl.x[:tokens],
+                                      query_start_loc=np.array([0, tokens], dtype=np.int32))
+            set_bytes = tokens * (wl.row_stride + wl.dim) * 2
+            result["context_sweep"][str(tokens)] = time_config(
+                kd, torch, sub, steps=100, warmup=10, sets=max(2, -(-(600 << 20) // set_bytes)))
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_runs)
     print(json.dumps(result), flush=True)
