@@ -62,7 +62,7 @@ constexpr int kShort = 4;
 constexpr int kHalf = 8;
 // The launch's last row blocks are split so that about this many waves compute
 // half tiles and, after them, this many quarter tiles (for 18 column blocks: the
-// last 1024 rows in 8-row parts, then the last 256 in 4-row parts).
+// 1024 rows before the last 256 in 8-row parts, and those 256 in 4-row parts).
 constexpr int kHalfTileWaves = 2304;
 constexpr int kQuarterTileWaves = 1152;
 constexpr int kMinWaves = 4;  // occupancy target (waves per SIMD)

@@ -111,8 +111,8 @@ def test_every_row_exactly_once(R, col_blocks):
 
 def test_one_long_sequence():
     """16384 tokens over 18 column blocks: 943 whole tiles, 64 tiles in halves and 16
-    in quarters after the first tile, i.e. the last 1024 rows in 8-row parts and the
-    256 before the end in 4-row parts."""
+    in quarters after the first tile, i.e. rows 15104-16127 in 8-row parts and the last
+    256 rows in 4-row parts."""
     qsl = np.array([0, 16384])
     got = _parts_by_map(qsl, 16384, 16, 18)
     assert got[0] == (0, 0, 16, 0)
