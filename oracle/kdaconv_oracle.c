@@ -42,6 +42,8 @@
  *   - a sequence whose cache line is the null block runs from zero history and
  *     neither reads nor writes the state; has_initial_state false runs from
  *     zero history and still writes the state;
+ *   - a cache line outside [0, num_cache_lines) names no line, and the sequence
+ *     is treated like a null-block sequence (zero history, no state access);
  *   - a zero-length sequence does nothing.
  *
  * Build: gcc -O2 -ffp-contract=off -fno-fast-math (see oracle/__init__.py).
@@ -271,7 +273,8 @@ static float conv_acc(const float* w, int64_t ws1, const float* bias_c,
  *              conv_states[l * cs_stride0 + c * cs_stride1 + k * cs_stride2];
  *              updated in place.
  * query_start_loc: int32 (num_seqs + 1), sequence s owns rows [qsl[s], qsl[s+1]).
- * cache_indices:   int32, the line of sequence s at cache_indices[s * ci_stride].
+ * cache_indices:   int32, the line of sequence s at cache_indices[s * ci_stride];
+ *                  a value outside [0, num_cache_lines) acts as the null block.
  * has_initial_state: one byte per sequence, nonzero = start from the stored state;
  *                    NULL = no sequence has one.
  * out:         words of format fmt (uint16 for bf16 and fp16, uint32 for FP32),
@@ -294,9 +297,6 @@ int oracle_packed_causal_conv1d(
   for (int64_t s = 0; s < num_seqs; ++s) {
     int64_t start = query_start_loc[s], end = query_start_loc[s + 1];
     if (start < 0 || end < start || end > num_tokens) return ORACLE_EINVAL;
-    int64_t line = cache_indices[s * ci_stride];
-    int live = !(has_null_block && line == null_block_id);
-    if (live && end > start && (line < 0 || line >= num_cache_lines)) return ORACLE_EINVAL;
   }
 
   for (int64_t s = 0; s < num_seqs; ++s) {
@@ -304,7 +304,7 @@ int oracle_packed_causal_conv1d(
     int64_t len = end - start;
     if (len == 0) continue; /* nothing to convolve, state untouched */
     int64_t line = cache_indices[s * ci_stride];
-    int live = !(has_null_block && line == null_block_id);
+    int live = !(has_null_block && line == null_block_id) && line >= 0 && line < num_cache_lines;
     int init = live && has_initial_state && has_initial_state[s];
     for (int64_t c = 0; c < dim; ++c) {
       float hist[3] = {0.0f, 0.0f, 0.0f}; /* e[t-3], e[t-2], e[t-1] */

@@ -63,8 +63,10 @@ def brute_force(wl: Workload):
         if end == start:
             continue
         line = int(wl.cache_indices[s])
-        live = not (wl.null_block_id is not None and line == wl.null_block_id)
-        init = live and bool(wl.has_initial_state[s])
+        # a line outside the state array names no line: like the null block
+        live = (not (wl.null_block_id is not None and line == wl.null_block_id)
+                and 0 <= line < wl.num_cache_lines)
+        init = live and wl.has_initial_state is not None and bool(wl.has_initial_state[s])
         for c in range(dim):
             e = [float(v) for v in st[line, c]] if init else [0.0, 0.0, 0.0]
             e += [float(v) for v in xf[start:end, c]]
