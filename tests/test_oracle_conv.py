@@ -278,11 +278,81 @@ def test_rejects_bad_metadata(olib):
     with pytest.raises(ValueError):
         oracle.packed_causal_conv1d(wl.x, 16, wl.weight, wl.bias, wl.conv_states.copy(), bad,
                                     wl.cache_indices, wl.has_initial_state, 8, lib=olib)
-    ci = wl.cache_indices.copy()
-    ci[0] = wl.num_cache_lines
-    with pytest.raises(ValueError):
-        oracle.packed_causal_conv1d(wl.x, 16, wl.weight, wl.bias, wl.conv_states.copy(),
-                                    wl.query_start_loc, ci, wl.has_initial_state, 8, lib=olib)
+
+
+@pytest.mark.parametrize("bad_line", [-1, -2 ** 31, 3, 2 ** 31 - 1])
+def test_out_of_range_line_acts_as_null_block(olib, bad_line):
+    """A cache line outside [0, lines) names no line: the sequence runs from zero history,
+    reads and writes no state, and its outputs are still written (the reading shared with
+    the null block). Checked against the exact brute force and against the same call with
+    that sequence on the null block."""
+    wl = make_workload([4, 6, 2], dim=16, part_dim=8, seed=52, init=[True, True, True],
+                       cache_indices=[1, bad_line, 0], lines=3)
+    before = wl.conv_states.copy()
+    got, st = _run(wl, olib)
+    want, want_st = brute_force(wl)
+    assert np.array_equal(got, want)
+    assert np.array_equal(st.view(np.uint32), want_st.view(np.uint32))
+    assert np.array_equal(st[2], before[2])  # the line no sequence names stays as it was
+    nul = make_workload([4, 6, 2], dim=16, part_dim=8, seed=52, init=[True, True, True],
+                        cache_indices=[1, 2, 0], lines=3, null_block_id=2)
+    got_n, st_n = _run(nul, olib)
+    assert np.array_equal(got, got_n)
+    assert np.array_equal(st.view(np.uint32), st_n.view(np.uint32))
+
+
+# ---------------------------------------------------------------- argument strides
+
+def _replaced(wl, **kw):
+    import dataclasses
+
+    return dataclasses.replace(wl, conv_states=wl.conv_states.copy(), **kw)
+
+
+@pytest.mark.parametrize("layout", ["transposed", "padded"])
+def test_weight_strides_against_brute_force(olib, layout):
+    """Tap k of channel c is read at weight[c * ws0 + k * ws1] for any two strides (page:
+    the launch passes both weight strides). A (dim, 4) view of a (4, dim) array (strides
+    1 and dim) and a view with a row pitch of 7 give the brute-force result, which reads
+    the same values without strides."""
+    wl = make_workload([5, 3, 8], dim=12, part_dim=4, seed=80, init=[True, False, True], lines=4)
+    want, want_st = brute_force(wl)
+    if layout == "transposed":
+        view = np.ascontiguousarray(wl.weight.T).T
+        assert view.strides == (4, 4 * 12)
+    else:
+        pad = np.full((12, 7), np.float32(1e30))
+        pad[:, 2:6] = wl.weight
+        view = pad[:, 2:6]
+        assert view.strides == (28, 4)
+    got, st = _run(_replaced(wl, weight=view), olib)
+    assert np.array_equal(got, want)
+    assert np.array_equal(st.view(np.uint32), want_st.view(np.uint32))
+
+
+def test_cache_index_stride_against_brute_force(olib):
+    """The line of sequence s is read at cache_indices[s * stride]: every other entry of an
+    array whose other entries name different, valid lines."""
+    wl = make_workload([5, 3, 8, 2], dim=8, part_dim=8, seed=81, init=[True, True, False, True],
+                       cache_indices=[3, 0, 5, 1], lines=7)
+    want, want_st = brute_force(wl)
+    inter = np.array([3, 6, 0, 2, 5, 4, 1, 6], dtype=np.int32)
+    view = inter[::2]
+    assert view.strides == (8,) and np.array_equal(view, wl.cache_indices)
+    got, st = _run(_replaced(wl, cache_indices=view), olib)
+    assert np.array_equal(got, want)
+    assert np.array_equal(st.view(np.uint32), want_st.view(np.uint32))
+
+
+def test_no_initial_state_array_means_none_set(olib):
+    """has_initial_state = None (a NULL pointer in the C call): every sequence starts from
+    zeros and still writes its line, as with an all-false array."""
+    wl = make_workload([5, 3, 8], dim=8, part_dim=8, seed=82, init=[True, True, True], lines=4)
+    got, st = _run(_replaced(wl, has_initial_state=None), olib)
+    wl.has_initial_state[:] = False
+    want, want_st = brute_force(wl)
+    assert np.array_equal(got, want)
+    assert np.array_equal(st.view(np.uint32), want_st.view(np.uint32))
 
 
 # ---------------------------------------------------------------- library form

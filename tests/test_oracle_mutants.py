@@ -35,8 +35,17 @@ MUTANTS = {
     "state written newest first": [("k * cs_stride2] = hist[k];", "k * cs_stride2] = hist[2 - k];")],
     "state never read": [("int init = live && has_initial_state && has_initial_state[s];",
                           "int init = 0;")],
-    "null block ignored": [("int live = !(has_null_block && line == null_block_id);\n    int init",
-                            "int live = 1;\n    int init")],
+    "null block ignored": [("int live = !(has_null_block && line == null_block_id) && line >= 0",
+                            "int live = 1 && line >= 0")],
+    "weight strides taken as contiguous": [("const float* w = weight + c * w_stride0;",
+                                            "const float* w = weight + c * 4;"),
+                                           ("conv_acc(w, w_stride1, b, hist, cur)",
+                                            "conv_acc(w, 1, b, hist, cur)")],
+    "cache index stride ignored": [("int64_t line = cache_indices[s * ci_stride];",
+                                    "int64_t line = cache_indices[s];")],
+    "missing initial-state array read as all set": [
+        ("int init = live && has_initial_state && has_initial_state[s];",
+         "int init = live && (!has_initial_state || has_initial_state[s]);")],
     "window shift wrong": [("hist[0] = hist[1];\n        hist[1] = hist[2];",
                             "hist[1] = hist[2];\n        hist[0] = hist[1];")],
     "planes transposed": [("int64_t o = (plane * num_tokens + t) * part_dim + col;",
@@ -70,6 +79,11 @@ PINS = [
     ("plane layout", conv_pins.test_plane_layout),
     ("state last three", lambda lib: conv_pins.test_state_is_last_three_inputs(lib, True)),
     ("null block", conv_pins.test_null_block_runs_from_zero_and_leaves_its_line),
+    *[(f"weight strides {l}", lambda lib, l=l: conv_pins.test_weight_strides_against_brute_force(lib, l))
+      for l in ("transposed", "padded")],
+    ("cache index stride", conv_pins.test_cache_index_stride_against_brute_force),
+    ("no initial-state array", conv_pins.test_no_initial_state_array_means_none_set),
+    ("out-of-range line", lambda lib: conv_pins.test_out_of_range_line_acts_as_null_block(lib, 3)),
     ("torch conv1d silu", lambda lib: conv_pins.test_against_torch_conv1d_float64(lib, 0, True)),
     ("silu random", act_pins.test_silu_random_against_exact),
     ("silu near midpoints", act_pins.test_silu_near_bf16_midpoints),
