@@ -50,16 +50,12 @@ namespace kdaconv {
 namespace {
 
 constexpr int kWave = 64;
-constexpr int kGroup = 1;  // rows sharing one rare-path branch (divides R)
 constexpr int kLaneChannels = 4;  // channels per lane
 // Tiles of at most this many rows (short sequences, a sequence's last rows) take a
 // path that loads only kShort rows. On 4096 sequences of 1-4 tokens it measured 15 %
 // faster than loading all R rows; 8 rows gained half as much; longer workloads are
 // unchanged.
 constexpr int kShort = 4;
-// Rows of the second reduced copy of the tile code (half tiles of the bf16 and
-// fp16 launches).
-constexpr int kHalf = 8;
 // The launch's last row blocks are split so that about this many waves compute
 // half tiles and, after them, this many quarter tiles (for 18 column blocks: the
 // 1024 rows before the last 256 in 8-row parts, and those 256 in 4-row parts).
@@ -381,17 +377,13 @@ __device__ __forceinline__ Tile describe_tile(const ConvParams& P, int p, int la
 }
 
 // The per-wave part of the convolution shared by the prefill and decode kernels:
-// the lane's channels, its weights and bias, the state line's I/O, the processing
-// of one prefill tile whose x rows were loaded by issue(), and decode steps.
+// the lane's channels, its weights and bias, the state line's I/O, prefill tiles
+// and decode steps.
 template <int kF, int V, int R, bool kBias, bool kSilu>
 struct ConvWorker {
   static constexpr int kBytes = element_bytes<kF>();
   typedef Lane<V * kBytes> L;
   typedef typename L::vec vec;
-  // x rows of a tile as loaded: 3 history rows, then R tile rows.
-  template <int RR>
-  using RowsOf = vec[3 + RR];
-  typedef RowsOf<R> Rows;
 
   const ConvParams& P;
   int lane;
@@ -617,125 +609,136 @@ struct ConvWorker {
     }
   }
 
-  // Issues the loads of a valid tile's x rows: always 3 history rows (the first
-  // row again when the tile has no history) and R tile rows (rows past the
-  // tile's end repeat its last row), so the number of loads never depends on the
-  // tile and every load is in bounds. Tile rows are streamed, except the last
-  // three, which the next tile of the column block reads again as its history.
-  template <int RR>
-  __device__ __forceinline__ void issue(RowsOf<RR>& buf, const Tile& d) {
-    const __amdgpu_buffer_rsrc_t xr =
-        make_rsrc(P.x + (int64_t)(d.t0 - d.halo) * P.x_row_stride * kBytes);
+  // Makes the compiler treat the values as used here, so that the wait for the loads
+  // that produce them is placed here and not deferred to a later point.
+  __device__ __forceinline__ static void pin(float (&f)[V]) {
 #pragma unroll
-    for (int r = 0; r < 3; ++r)
-      buf[r] = L::template load<kKeep>(xr, xvo, d.halo ? (uint32_t)r * xrow_bytes : 0u);
-#pragma unroll
-    for (int r = 0; r < RR; ++r) {
-      const uint32_t off = (uint32_t)(min(r, d.n - 1) + d.halo) * xrow_bytes;
-      buf[3 + r] = r < RR - 3 ? L::template load<kStream>(xr, xvo, off)
-                              : L::template load<kKeep>(xr, xvo, off);
-    }
+    for (int k = 0; k < V; ++k) asm volatile("" : "+v"(f[k]));
   }
 
-  // Processes a valid tile whose rows issue() loaded into buf.
-  template <int RR>
-  __device__ __forceinline__ void compute(RowsOf<RR>& buf, const Tile& d) {
-    // History e[t0-3], e[t0-2], e[t0-1]: x rows for later tiles; for the first tile
-    // of a sequence the stored state if the sequence is live and has an initial
-    // state, else zeros.
+  // One valid tile of at most RR rows: loads, history, taps, activation, stores, and
+  // (first tile of a sequence, kFirst) the state update.
+  //
+  // Loads. Vector memory operations complete in issue order and the compiler waits
+  // for each row just before its arithmetic, so every row is computed as soon as it
+  // has arrived while the later rows are still on their way. A later tile therefore
+  // issues its 3 history rows first, then its RR rows, and takes its history as soon
+  // as those three have arrived. A first tile issues its rows first, then reads the
+  // sequence's line and state (a dependent chain that should not delay the rows) and
+  // waits for everything before its first row. The two orders are separate copies of
+  // the code (kFirst): joined, the compiler would have to assume the slower one and
+  // wait for all rows before the first row of every tile. All RR row loads are always
+  // issued (rows past the tile's end repeat its last row), so their count does not
+  // depend on the tile. Tile rows are streamed, except the last three, which the next
+  // tile of the column block reads again as its history.
+  //
+  // Nothing is called inside the row loop: a call there would keep every live value
+  // (weights, history, rows in flight) in registers the callee preserves, raising
+  // the register count and with it cutting the waves per SIMD, or would put them on
+  // the stack. Elements that need the exact path are appended to the list; if a tile
+  // has more of them than the list holds, the tile is rewritten after its rows
+  // (redo_tile).
+  template <int RR, bool kFirst>
+  __device__ __forceinline__ void tile(const Tile& d) {
+    vec rows[RR];
     float h0[V], h1[V], h2[V];
     bool live = false;
     int64_t line = 0;
-    if (d.halo) {
-      unpack<kF, V>(buf[0], h0);
-      unpack<kF, V>(buf[1], h1);
-      unpack<kF, V>(buf[2], h2);
+    const __amdgpu_buffer_rsrc_t xr =
+        make_rsrc(P.x + (int64_t)(d.t0 - d.halo) * P.x_row_stride * kBytes);
+    auto issue_rows = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int r = 0; r < RR; ++r) {
+        const uint32_t off = (uint32_t)(min(r, d.n - 1) + d.halo) * xrow_bytes;
+        rows[r] = r < RR - 3 ? L::template load<kStream>(xr, xvo, off)
+                             : L::template load<kKeep>(xr, xvo, off);
+      }
+    };
+    if (!kFirst) {
+      // History e[t0-3], e[t0-2], e[t0-1]: the 3 rows before the tile.
+      vec hv[3];
+#pragma unroll
+      for (int r = 0; r < 3; ++r) hv[r] = L::template load<kKeep>(xr, xvo, (uint32_t)r * xrow_bytes);
+      issue_rows();
+      __builtin_amdgcn_sched_barrier(0);  // the history is unpacked after all issues
+      unpack<kF, V>(hv[0], h0);
+      unpack<kF, V>(hv[1], h1);
+      unpack<kF, V>(hv[2], h2);
+      pin(h0);
+      pin(h1);
+      pin(h2);
     } else {
+      issue_rows();
+      // History: the stored state if the sequence is live and has an initial state,
+      // else zeros.
       line = P.cache_indices[(int64_t)d.s * P.ci_stride];
       live = !(P.has_null_block && line == P.null_block_id) && line >= 0 &&
              line < P.num_cache_lines;
       const bool init = live && P.has_init != nullptr && P.has_init[d.s] != 0;
       if (init) {
         load_state(line, h0, h1, h2);
+        pin(h0);
+        pin(h1);
+        pin(h2);
       } else {
 #pragma unroll
         for (int k = 0; k < V; ++k) h0[k] = h1[k] = h2[k] = 0.0f;
       }
     }
 
-    auto fix_store = [&](uint32_t word, uint32_t offset) __attribute__((always_inline)) {
-      store_word(word, offset);
-    };
-
-    // Rows r0 .. r0 + kGroup - 1 of the tile, of which the first `rows` exist:
-    // taps, activation, stores, history shift. The rows share one rare-path
-    // branch, so their independent arithmetic can interleave.
-    auto group = [&](int r0, int rows) __attribute__((always_inline)) {
-      float acc[kGroup][V];
+    bool overflow = false;  // wave-uniform
+    // Row r of the tile: taps, activation, store, history shift, and the elements
+    // whose fast word may be wrong recorded in the list.
+    auto row = [&](int r) __attribute__((always_inline)) {
+      float xv[V], acc[1][V];
+      unpack<kF, V>(rows[r], xv);
 #pragma unroll
-      for (int g = 0; g < kGroup; ++g) {
-        float xv[V];
-        unpack<kF, V>(buf[3 + r0 + g], xv);
-#pragma unroll
-        for (int k = 0; k < V; ++k) {
-          float a = bs[k];
-          a = __builtin_fmaf(w0[k], h0[k], a);
-          a = __builtin_fmaf(w1[k], h1[k], a);
-          a = __builtin_fmaf(w2[k], h2[k], a);
-          a = __builtin_fmaf(w3[k], xv[k], a);
-          acc[g][k] = a;
-        }
-        if (g < rows) {
-#pragma unroll
-          for (int k = 0; k < V; ++k) {
-            h0[k] = h1[k];
-            h1[k] = h2[k];
-            h2[k] = xv[k];
-          }
-        }
+      for (int k = 0; k < V; ++k) {
+        float a = bs[k];
+        a = __builtin_fmaf(w0[k], h0[k], a);
+        a = __builtin_fmaf(w1[k], h1[k], a);
+        a = __builtin_fmaf(w2[k], h2[k], a);
+        a = __builtin_fmaf(w3[k], xv[k], a);
+        acc[0][k] = a;
+        h0[k] = h1[k];
+        h1[k] = h2[k];
+        h2[k] = xv[k];
       }
       constexpr int kWords = row_words<kF, V>();
-      uint32_t words[kGroup][kWords];
-      float y[kGroup][V];
-      uint32_t aux[kGroup][V];
-      const bool check = activate_rows<kF, kSilu, V, kGroup>(acc, y, aux, words);
+      uint32_t words[1][kWords];
+      float y[1][V];
+      uint32_t aux[1][V];
+      const bool check = activate_rows<kF, kSilu, V, 1>(acc, y, aux, words);
+      vec o;
 #pragma unroll
-      for (int g = 0; g < kGroup; ++g) {
-        if (g < rows) {
-          vec o;
-#pragma unroll
-          for (int i = 0; i < kWords; ++i) o[i] = words[g][i];
-          L::template store<kStream>(o, orsrc, ovo, (uint32_t)(d.t0 + r0 + g) * orow_bytes);
-        }
-      }
-      // Rare (any lane): record the elements whose fast word may be wrong; they
-      // are rewritten when the list is flushed.
+      for (int i = 0; i < kWords; ++i) o[i] = words[0][i];
+      const uint32_t ro = (uint32_t)(d.t0 + r) * orow_bytes;
+      L::template store<kStream>(o, orsrc, ovo, ro);
       if (__builtin_expect(__builtin_amdgcn_ballot_w64(check) != 0, 0)) {
-        if (!fix.fits(kGroup * V * kWave)) fix.template flush<kF, kSilu>(lane, fix_store);
+        if (!fix.fits(V * kWave)) {
+          overflow = true;
+        } else {
 #pragma unroll
-        for (int g = 0; g < kGroup; ++g) {
-          if (g < rows) {
-#pragma unroll
-            for (int k = 0; k < V; ++k)
-              fix.append(needs_exact<kF, kSilu>(acc[g][k], y[g][k], aux[g][k]), acc[g][k],
-                         ovo + (uint32_t)(kBytes * k) + (uint32_t)(d.t0 + r0 + g) * orow_bytes);
-          }
+          for (int k = 0; k < V; ++k)
+            fix.append(needs_exact<kF, kSilu>(acc[0][k], y[0][k], aux[0][k]), acc[0][k],
+                       ovo + (uint32_t)(kBytes * k) + ro);
         }
       }
     };
     if (d.n == RR) {
       // Full tile: straight-line code, no conditions.
 #pragma unroll
-      for (int r0 = 0; r0 < RR; r0 += kGroup) group(r0, kGroup);
+      for (int r = 0; r < RR; ++r) row(r);
     } else {
 #pragma unroll
-      for (int r0 = 0; r0 < RR; r0 += kGroup)
-        if (r0 < d.n) group(r0, min(kGroup, d.n - r0));
+      for (int r = 0; r < RR; ++r)
+        if (r < d.n) row(r);
     }
+    if (__builtin_expect(overflow, 0)) redo_tile(d, line, live);
 
     // Updated state: the last three values of (history ++ x) for this sequence,
     // written by the sequence's first tile after its reads.
-    if (d.j == 0 && live && active) {
+    if (kFirst && live && active) {
       if (d.t0 + d.n < d.end) {
         // The sequence continues past this tile: its last rows are end-3 .. end-1.
         const __amdgpu_buffer_rsrc_t tr = make_rsrc(P.x + (int64_t)(d.end - 3) * P.x_row_stride * kBytes);
@@ -744,6 +747,49 @@ struct ConvWorker {
         unpack<kF, V>(L::template load<kKeep>(tr, xvo, 2 * xrow_bytes), h2);
       }
       store_state(line, h0, h1, h2);
+    }
+  }
+
+  // Element c of row t of x, widened.
+  __device__ __forceinline__ float x_at(int64_t t, int c) const {
+    const char* rowp = P.x + t * P.x_row_stride * kBytes;
+    if (kF == kF32) return reinterpret_cast<const float*>(rowp)[c];
+    return widen_half<kF>(reinterpret_cast<const uint16_t*>(rowp)[c], 0);
+  }
+
+  // Rare: more elements of the tile needed the exact path than the list holds (only
+  // tiles full of values next to rounding boundaries, or of NaN or infinity). The
+  // list is flushed, then every element of the tile is rewritten with its exact
+  // word, one at a time and with every operand loaded again just before its use, so
+  // that only the loop's indices are live across the call of the exact evaluation.
+  // It runs before the first tile's state update, so the state line it reads is the
+  // one the tile started from.
+  __device__ __forceinline__ void redo_tile(const Tile& d, int64_t line, bool live) {
+    auto fix_store = [&](uint32_t word, uint32_t offset) __attribute__((always_inline)) {
+      store_word(word, offset);
+    };
+    fix.template flush<kF, kSilu>(lane, fix_store);  // also waits for the tile's stores
+    const bool init = !d.halo && live && P.has_init != nullptr && P.has_init[d.s] != 0;
+#pragma unroll 1
+    for (int r = 0; r < d.n; ++r) {
+#pragma unroll 1
+      for (int k = 0; k < V; ++k) {
+        const int c = cl + k;
+        const float* wp = P.weight + (int64_t)c * P.w_stride0;
+        float a = kBias ? P.bias[c] : 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int rr = r - 3 + i;  // row of e relative to the tile's first row
+          float e;
+          if (rr >= 0 || d.halo)
+            e = x_at((int64_t)d.t0 + rr, c);
+          else
+            e = init ? P.states[line * P.cs_stride0 + (int64_t)c * P.cs_stride1 + (3 + rr) * P.cs_stride2]
+                     : 0.0f;
+          a = __builtin_fmaf(wp[i * P.w_stride1], e, a);
+        }
+        store_word(act_word_exact<kF>(a, kSilu), ovo + (uint32_t)(kBytes * k) + (uint32_t)(d.t0 + r) * orow_bytes);
+      }
     }
   }
 
@@ -783,22 +829,27 @@ __global__ __launch_bounds__(kWave * kG) __attribute__((amdgpu_waves_per_eu(kMin
   w.load_weights();
   const Tile d = describe_tile<R>(P, p, lane);
   if (!d.valid) return;
-  typedef ConvWorker<kF, V, R, kBias, kSilu> W;
-  if (kShort > 0 && d.n <= kShort) {
-    // A tile of at most kShort rows (short sequences, a sequence's last rows, the
-    // quarter tiles at the end of the launch): only those rows are loaded.
-    typename W::template RowsOf<kShort> buf;
-    w.template issue<kShort>(buf, d);
-    w.template compute<kShort>(buf, d);
-  } else if (R > kHalf && d.n <= kHalf) {
-    // Half tiles near the end of the launch (and short remainders).
-    typename W::template RowsOf<kHalf> buf;
-    w.template issue<kHalf>(buf, d);
-    w.template compute<kHalf>(buf, d);
+  // One copy of the tile code per size class: rows of short sequences and of a
+  // sequence's end, the half and quarter tiles at the end of the launch, whole
+  // tiles; each loads only the rows of its class.
+  constexpr int kQ = R / 4 > kShort ? R / 4 : kShort;
+  constexpr int kH = R / 2 > kQ ? R / 2 : kQ;
+  if (d.halo) {
+    if (d.n <= kShort)
+      w.template tile<kShort, false>(d);
+    else if (kQ > kShort && d.n <= kQ)
+      w.template tile<kQ, false>(d);
+    else if (kH > kQ && d.n <= kH)
+      w.template tile<kH, false>(d);
+    else
+      w.template tile<R, false>(d);
   } else {
-    typename W::Rows buf;
-    w.template issue<R>(buf, d);
-    w.template compute<R>(buf, d);
+    if (d.n <= kShort)
+      w.template tile<kShort, true>(d);
+    else if (kH > kShort && d.n <= kH)
+      w.template tile<kH, true>(d);
+    else
+      w.template tile<R, true>(d);
   }
   w.finish();
 }
