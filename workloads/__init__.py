@@ -268,6 +268,30 @@ def decode_batch(batch: int = 256, seed: int = 6, x_dtype: str = "bf16") -> Work
                     np.ones(batch, dtype=bool), 1536, "silu", None, x_dtype)
 
 
+def large_output_case(seed: int = 7) -> Workload:
+    """An output of 2.4 GB, beyond the 2 GiB a single launch addresses: 262144 tokens,
+    dim 4608 = 3 x 1536 contiguous (x is 2.4 GB as well), six sequences including lengths
+    1, 2 and 3, eight lines, mixed initial-state flags, bias, SiLU.
+
+    x is drawn as raw bf16 words (uniform random sign, exponent in [120, 127], mantissa
+    bits), i.e. magnitudes in [2^-7, 2), which is far cheaper than 1.2e9 normal draws;
+    every row differs, so a misplaced row offset shows."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    T, dim, lines = 262144, 4608, 8
+    raw = rng.integers(0, 1 << 16, size=(T, dim), dtype=np.uint16)
+    np.bitwise_and(raw, np.uint16(0x83FF), out=raw)
+    np.bitwise_xor(raw, np.uint16(0x3C00), out=raw)
+    lens = np.array([100003, 1, 2, 3, 62135, 100000])
+    assert int(lens.sum()) == T
+    w = _normal(rng, (dim, 4), 0.5)
+    b = _normal(rng, (dim,), 0.1)
+    st = _normal(rng, (lines, dim, 3), 1.0)
+    ci = rng.permutation(lines)[: len(lens)].astype(np.int32)
+    init = np.array([True, False, True, True, False, True])
+    return Workload("large output: 262144 tokens x 4608 channels, 6 seqs, contiguous",
+                    raw, dim, w, b, st, _qsl(lens), ci, init, 1536, "silu", None)
+
+
 CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}
 
 
