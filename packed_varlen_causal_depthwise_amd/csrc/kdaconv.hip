@@ -394,8 +394,13 @@ struct ConvWorker {
   float w0[V], w1[V], w2[V], w3[V], bs[V];
   FixupList<kFixCapacity> fix;
 
-  __device__ __forceinline__ ConvWorker(const ConvParams& params, int lane_, int cb, uint2* slots)
-      : P(params), lane(lane_), fix{slots, 0u} {
+  float* stage;  // the wave's LDS slice of 3 V kWave floats for state lines
+  int cfirst;  // first channel of the wave
+
+  __device__ __forceinline__ ConvWorker(const ConvParams& params, int lane_, int cb, uint2* slots,
+                                        float* stage_)
+      : P(params), lane(lane_), fix{slots, 0u}, stage(stage_) {
+    cfirst = P.col_begin + cb * kWave * V;
     const int c0 = P.col_begin + (cb * kWave + lane) * V;
     active = c0 < P.col_end;
     cl = active ? c0 : P.col_end - V;
@@ -535,10 +540,58 @@ struct ConvWorker {
     }
   }
 
+  // Staged write of entries 0, 1, 2 of the wave's channels of a contiguous (dim, 3)
+  // line. The wave's channels [cfirst, cfirst + n) are 12 n consecutive bytes of the
+  // line, and lane l's V channels are bytes [12 V l, 12 V (l + 1)) of that part.
+  // Written directly, each store instruction would cover every third 16-byte piece of
+  // the part, a third of each cache line it touches. Instead every lane writes its
+  // 3 V floats to the wave's own LDS slice at the same place, and each store
+  // instruction then takes 64 consecutive 16-byte pieces (1 KB) from the slice to the
+  // line (4096 decode steps at dim 4608: 121.6 -> 107.9 us). The buffer descriptor's
+  // range is the part's length, so pieces at or past its end, read by lanes past the
+  // launch's last channel, are dropped by the hardware; those lanes write the last
+  // active lane's slot, with its values. Only this wave uses its slice, and the LDS
+  // performs a wave's operations in order; the waits keep the compiler from moving
+  // slice accesses across each other and make each phase's writes complete before
+  // the next phase reads.
+  __device__ __forceinline__ static void slice_fence() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0) only (vmcnt and expcnt at their maxima)
+    asm volatile("" ::: "memory");
+  }
+  __device__ __forceinline__ void store_state_staged(int64_t line, const float (&h0)[V],
+                                                     const float (&h1)[V], const float (&h2)[V]) const {
+    constexpr int kPieces = 3 * V / 4;  // 16-byte pieces per lane
+    u32x4* s4 = reinterpret_cast<u32x4*>(stage);
+    const int slot = (cl - cfirst) / V;
+    float f[3 * V];
+#pragma unroll
+    for (int k = 0; k < V; ++k) {
+      f[3 * k] = h0[k];
+      f[3 * k + 1] = h1[k];
+      f[3 * k + 2] = h2[k];
+    }
+    slice_fence();  // earlier reads of the slice are done
+#pragma unroll
+    for (int q = 0; q < kPieces; ++q) {
+      u32x4 t;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) t[e] = __float_as_uint(f[4 * q + e]);
+      s4[kPieces * slot + q] = t;
+    }
+    slice_fence();
+    const int n = min(kWave * V, P.col_end - cfirst);
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        P.states + line * P.cs_stride0 + (int64_t)cfirst * 3, (short)0, n * 12, kDescWord3);
+#pragma unroll
+    for (int q = 0; q < kPieces; ++q)
+      __builtin_amdgcn_raw_buffer_store_b128(s4[lane + kWave * q], r, (uint32_t)(lane + kWave * q) * 16u, 0, kKeep);
+  }
+
   // Decode steps of sequences s0 .. s0 + kSeq - 1 (those below num_seqs): all their
   // loads (cache lines, x rows, state lines) are issued before any arithmetic, then
   // each sequence is computed and stored in turn.
-  template <int kSeq>
+  template <int kSeq, bool kStaged>
   __device__ __forceinline__ void decode_many(int s0) {
     int64_t line[kSeq];
     bool live[kSeq];
@@ -605,7 +658,10 @@ struct ConvWorker {
 #pragma unroll
       for (int w = 0; w < kWords; ++w) o[w] = words[0][w];
       L::template store<kStream>(o, orsrc, ovo, (uint32_t)s * orow_bytes);
-      if (live[i] && active) store_state(line[i], h1[i], h2[i], xv);
+      if (kStaged && live[i])
+        store_state_staged(line[i], h1[i], h2[i], xv);
+      else if (live[i] && active)
+        store_state(line[i], h1[i], h2[i], xv);
     }
   }
 
@@ -738,7 +794,7 @@ struct ConvWorker {
 
     // Updated state: the last three values of (history ++ x) for this sequence,
     // written by the sequence's first tile after its reads.
-    if (kFirst && live && active) {
+    if (kFirst && live && (active || P.state_vec)) {
       if (d.t0 + d.n < d.end) {
         // The sequence continues past this tile: its last rows are end-3 .. end-1.
         const __amdgpu_buffer_rsrc_t tr = make_rsrc(P.x + (int64_t)(d.end - 3) * P.x_row_stride * kBytes);
@@ -746,7 +802,10 @@ struct ConvWorker {
         unpack<kF, V>(L::template load<kKeep>(tr, xvo, xrow_bytes), h1);
         unpack<kF, V>(L::template load<kKeep>(tr, xvo, 2 * xrow_bytes), h2);
       }
-      store_state(line, h0, h1, h2);
+      if (P.state_vec)
+        store_state_staged(line, h0, h1, h2);
+      else
+        store_state(line, h0, h1, h2);
     }
   }
 
@@ -825,7 +884,8 @@ __global__ __launch_bounds__(kWave * kG) __attribute__((amdgpu_waves_per_eu(kMin
   if (cb >= P.col_blocks) return;
   // Weights first: their loads overlap the search for the tile's sequence.
   __shared__ uint2 fix_slots[kG][kFixCapacity];
-  ConvWorker<kF, V, R, kBias, kSilu> w(P, lane, cb, fix_slots[wave]);
+  __shared__ float stage[kG][3 * V * kWave];
+  ConvWorker<kF, V, R, kBias, kSilu> w(P, lane, cb, fix_slots[wave], stage[wave]);
   w.load_weights();
   const Tile d = describe_tile<R>(P, p, lane);
   if (!d.valid) return;
@@ -865,9 +925,13 @@ __global__ __launch_bounds__(kWave * kG) void packed_conv_update_kernel(const Co
   const int p = slot.p;
   const int cb = slot.cb;
   if (cb >= P.col_blocks) return;
-  ConvWorker<kF, V, 1, kBias, kSilu> w(P, lane, cb, nullptr);
+  __shared__ float stage[kG][3 * V * kWave];
+  ConvWorker<kF, V, 1, kBias, kSilu> w(P, lane, cb, nullptr, stage[wave]);
   w.load_weights();
-  w.template decode_many<kSeq>(p * kSeq);
+  if (P.state_vec)
+    w.template decode_many<kSeq, true>(p * kSeq);
+  else
+    w.template decode_many<kSeq, false>(p * kSeq);
 }
 
 // The activation map on consecutive FP32 bit patterns, 8 per lane as two rows of 4,
@@ -1025,15 +1089,15 @@ void launch_update_seq(ConvParams P, bool bias, bool silu, hipStream_t st) {
 }
 
 // Sequences per decode wave: as many as keep at least 2048 waves in the launch (two per
-// SIMD). Interleaved timing at dim 4608: 1024 sequences 35.5 -> 31.4 us with 8 per
-// wave; 256 sequences 12.0 -> 11.8 us with 2; 64 sequences unchanged with 1.
+// SIMD), at most 4. Interleaved timing at dim 4608: 1024 sequences 35.5 -> 31.4 us with
+// several sequences per wave instead of one; 256 sequences 12.0 -> 11.8 us with 2; 64
+// sequences unchanged with 1. Eight sequences per wave need about 180 VGPRs, two waves
+// per SIMD: 4096 sequences took 113.6 us with eight and 107.9 us with four.
 template <int kF, int V>
 void launch_update(ConvParams P, int64_t cols, bool bias, bool silu, hipStream_t st) {
   P.col_blocks = (int32_t)((cols / V + kWave - 1) / kWave);
   const int64_t waves1 = (int64_t)P.num_seqs * P.col_blocks;
-  if (waves1 >= 8 * 2048)
-    launch_update_seq<kF, V, 8>(P, bias, silu, st);
-  else if (waves1 >= 4 * 2048)
+  if (waves1 >= 4 * 2048)
     launch_update_seq<kF, V, 4>(P, bias, silu, st);
   else if (waves1 >= 2 * 2048)
     launch_update_seq<kF, V, 2>(P, bias, silu, st);
