@@ -724,13 +724,25 @@ struct ConvWorker {
       pin(h1);
       pin(h2);
     } else {
-      issue_rows();
       // History: the stored state if the sequence is live and has an initial state,
-      // else zeros.
-      line = P.cache_indices[(int64_t)d.s * P.ci_stride];
+      // else zeros. The line and the flag are requested before the rows, so that
+      // waiting for them does not wait for the rows as well (vector loads complete in
+      // order); the state, which depends on them, is requested while the rows are on
+      // their way. They are loaded at a lane offset the compiler cannot see is zero,
+      // so it keeps them as per-lane values and waits for them only where they are
+      // made wave-uniform, after the rows have been issued.
+      int vzero;
+      asm volatile("v_mov_b32 %0, 0" : "=v"(vzero));
+      const int32_t line_v = __builtin_amdgcn_raw_buffer_load_b32(
+          make_rsrc(P.cache_indices + (int64_t)d.s * P.ci_stride), (uint32_t)vzero, 0, kKeep);
+      const uint32_t init_v = P.has_init != nullptr
+          ? __builtin_amdgcn_raw_buffer_load_b8(make_rsrc(P.has_init + d.s), (uint32_t)vzero, 0, kKeep)
+          : 0u;
+      issue_rows();
+      line = __builtin_amdgcn_readfirstlane(line_v);
       live = !(P.has_null_block && line == P.null_block_id) && line >= 0 &&
              line < P.num_cache_lines;
-      const bool init = live && P.has_init != nullptr && P.has_init[d.s] != 0;
+      const bool init = live && __builtin_amdgcn_readfirstlane(init_v) != 0;
       if (init) {
         load_state(line, h0, h1, h2);
         pin(h0);
