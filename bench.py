@@ -236,6 +236,81 @@ def device_info(torch, dev) -> dict:
             "memory_gib": round(props.total_memory / 2**30, 1)}
 
 
+class ClockSampler:
+    """Polls the GPU's core (GFX) and memory clocks in a background thread through amdsmi
+    (the interface torch.cuda.clock_rate uses on ROCm), every 5 ms while sampling is
+    on: over the settle phase and the spread blocks of the headline workload, which
+    bracket the timed region. It is paused during the timed region itself, where the
+    thread's turns at the interpreter lock could delay the launches. Best effort: if
+    amdsmi is missing or refuses, the error is reported instead."""
+
+    def __init__(self, torch, dev, period_s: float = 0.005):
+        import threading
+
+        self.period = period_s
+        self.samples = {"gfx": [], "mem": []}
+        self.error = None
+        self._on = threading.Event()
+        self._stop = threading.Event()
+        self._thread = None
+        try:
+            import amdsmi
+
+            self._amdsmi = amdsmi
+            self._handle = torch.cuda._get_amdsmi_handler(dev)
+            self._read(keep=False)
+        except Exception as e:  # noqa: BLE001 - reported, not raised
+            self.error = f"{type(e).__name__}: {e}"
+            return
+        self._thread = threading.Thread(target=self._run, daemon=True)
+        self._thread.start()
+
+    def _read(self, keep: bool = True):
+        a = self._amdsmi
+        for key, kind in (("gfx", a.AmdSmiClkType.GFX), ("mem", a.AmdSmiClkType.MEM)):
+            v = a.amdsmi_get_clock_info(self._handle, kind).get("clk")
+            if keep and isinstance(v, (int, float)):
+                self.samples[key].append(float(v))
+
+    def _run(self):
+        while not self._stop.is_set():
+            self._on.wait(0.05)
+            if self._stop.wait(self.period) or not self._on.is_set():
+                continue
+            try:
+                self._read()
+            except Exception as e:  # noqa: BLE001
+                self.error = f"{type(e).__name__}: {e}"
+                return
+
+    def resume(self):
+        self._on.set()
+
+    def pause(self):
+        self._on.clear()
+
+    def stop(self):
+        self._on.clear()
+        self._stop.set()
+        if self._thread is not None:
+            self._thread.join()
+
+    def report(self) -> dict:
+        if self.error and not self.samples["gfx"]:
+            return {"error": self.error}
+        out = {"source": "amdsmi_get_clock_info, polled every 5 ms",
+               "window": "the settle phase and the spread blocks of the headline workload "
+                         "(paused during the timed region between them)"}
+        for key in ("gfx", "mem"):
+            v = np.array(self.samples[key])
+            if v.size:
+                out[f"{key}_mhz"] = {"median": float(np.median(v)), "min": float(v.min()),
+                                     "max": float(v.max()), "samples": int(v.size)}
+        if self.error:
+            out["error"] = self.error
+        return out
+
+
 def oracle_on_channel_slices(oracle, wl, threads: int):
     """The oracle on `threads` channel slices of the workload at once (Python threads;
     ctypes releases the interpreter lock during the C call). A channel's outputs and
@@ -382,7 +457,10 @@ def main() -> int:
     for i in range(args.warmup):
         step(i)
     first_us = back_to_back(torch, stream, step, args.steps, 1)[0]
+    clocks = ClockSampler(torch, dev)
+    clocks.resume()
     settled = settle(torch, step, args.settle_ms)
+    clocks.pause()
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize(dev)
@@ -402,7 +480,9 @@ def main() -> int:
 
     # Spread: more blocks of K back-to-back steps timed the same way, one per-launch mean
     # per block.
+    clocks.resume()
     blocks_us = back_to_back(torch, stream, step, args.steps, args.spread_blocks)
+    clocks.stop()
 
     value = nbytes / (ms_per_step * 1e-3) / 1e9
     result = {
@@ -422,6 +502,7 @@ def main() -> int:
         "dtype": "bf16",
         "data": "synthetic",
         "device": device_info(torch, dev),
+        "clocks": clocks.report(),
         "config": {
             "workload": "packed varlen causal depthwise conv: 1 sequence x 16384 tokens, "
                         "dim 4608 = 3 x 1536, bf16 x read in place from rows of 9728, bf16 "

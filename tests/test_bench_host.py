@@ -35,3 +35,21 @@ def test_more_than_one_gpu_is_refused():
                        text=True, timeout=120)
     assert r.returncode == 2
     assert "single GPU" in r.stderr
+
+
+def test_clock_sampler_reports_instead_of_raising():
+    """Without a GPU (or amdsmi) the sampler reports the error and the bench goes on; with
+    samples it reports their median, minimum and maximum."""
+    import torch
+
+    s = bench.ClockSampler(torch, torch.device("cuda:0"))
+    s.resume()
+    s.pause()
+    s.stop()
+    rep = s.report()
+    assert ("error" in rep) or ("gfx_mhz" in rep)
+    s.samples = {"gfx": [2400.0, 2100.0, 2300.0], "mem": [1900.0]}
+    s.error = None
+    rep = s.report()
+    assert rep["gfx_mhz"] == {"median": 2300.0, "min": 2100.0, "max": 2400.0, "samples": 3}
+    assert rep["mem_mhz"]["median"] == 1900.0
