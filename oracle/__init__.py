@@ -13,7 +13,9 @@ C file's header.
 Pins (tests/test_oracle_*.py): exhaustive bf16 rounding against torch's CPU
 conversion; fp16 rounding and widening against numpy's float16; the correctly rounded exp against mpmath; the SiLU map against exact
 rational arithmetic; the conv against exact-rational brute force, hand-derived
-golden cases, invariants, and PyTorch's float64 conv1d within its error bound.
+golden cases, invariants, and PyTorch's float64 conv1d within its error bound; the
+decode step with a bf16 state against exact-rational brute force with the weight and
+the state re-indexed by hand (tests/test_oracle_decode_bf16_state.py).
 """
 
 from __future__ import annotations
@@ -91,6 +93,15 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
         vp,  # out
     ]
     lib.oracle_packed_causal_conv1d.restype = i32
+    lib.oracle_packed_causal_conv1d_update_bf16_state.argtypes = [
+        vp, i64, i64, i64,  # x, batch, dim, x_row_stride
+        vp, i64, i64, i64, vp,  # weight, part stride, channel stride, width stride, bias
+        vp, i64, i64, i64, i64,  # conv_states (bf16 words), lines, strides
+        vp, i64,  # cache_indices, ci_stride
+        i64, i32, i32, i64,  # part_dim, silu, has_null_block, null_block_id
+        vp,  # out
+    ]
+    lib.oracle_packed_causal_conv1d_update_bf16_state.restype = i32
     return lib
 
 
@@ -233,6 +244,60 @@ def packed_causal_conv1d_update(x: np.ndarray, dim: int, weight: np.ndarray,
     return packed_causal_conv1d(x, dim, weight, bias, conv_states, qsl, cache_indices, init,
                                 part_dim, activation, null_block_id, out=out, lib=lib,
                                 x_dtype=x_dtype)
+
+
+def weight_strides(weight: np.ndarray, part_dim: int):
+    """(part stride, channel stride, width stride) in elements of an FP32 weight given
+    either as the prefill page's (dim, 4) [channel, width] array or as the decode page's
+    width-major (parts, 4, part_dim) [part, width, channel] array (any strides)."""
+    assert weight.dtype == np.float32
+    e = weight.itemsize
+    if weight.ndim == 2:
+        assert weight.shape[1] == 4
+        return part_dim * weight.strides[0] // e, weight.strides[0] // e, weight.strides[1] // e
+    assert weight.ndim == 3 and weight.shape[1:] == (4, part_dim)
+    return weight.strides[0] // e, weight.strides[2] // e, weight.strides[1] // e
+
+
+def packed_causal_conv1d_update_bf16_state(x: np.ndarray, dim: int, weight: np.ndarray,
+                                           bias: Optional[np.ndarray], conv_states: np.ndarray,
+                                           cache_indices: np.ndarray, part_dim: int,
+                                           activation="silu",
+                                           null_block_id: Optional[int] = None,
+                                           out: Optional[np.ndarray] = None,
+                                           lib=None) -> np.ndarray:
+    """The decode step with a bf16 conv state (page vllm.models.kimi_k3.amd.ops.kda_decode:
+    the fused decode kernel's bf16 input and bf16 state, and its width-major FP32 weight).
+
+    x: bf16 words (batch, row_stride), unit column stride; row b is sequence b's token.
+    weight: (dim, 4) [channel, width] or (dim // part_dim, 4, part_dim) width-major.
+    conv_states: bf16 words (uint16), logical (lines, dim, >= 3), any strides; updated in
+    place. Returns bf16 words (dim // part_dim, batch, part_dim)."""
+    lib = lib or load()
+    assert x.dtype == np.uint16 and x.ndim == 2 and x.strides[1] == 2
+    assert conv_states.dtype == np.uint16 and conv_states.ndim == 3
+    assert conv_states.shape[1] == dim and conv_states.shape[2] >= 3
+    assert cache_indices.dtype == np.int32
+    if bias is not None:
+        assert bias.dtype == np.float32 and bias.shape == (dim,) and bias.flags.c_contiguous
+    ps, s0, s1 = weight_strides(weight, part_dim)
+    assert weight.shape[0] * (part_dim if weight.ndim == 3 else 1) == dim
+    batch = x.shape[0]
+    if out is None:
+        out = np.zeros((dim // part_dim, batch, part_dim), dtype=np.uint16)
+    assert out.dtype == np.uint16 and out.flags.c_contiguous
+    assert out.shape == (dim // part_dim, batch, part_dim)
+    rc = lib.oracle_packed_causal_conv1d_update_bf16_state(
+        x.ctypes.data, batch, dim, x.strides[0] // 2,
+        weight.ctypes.data, ps, s0, s1, _ptr(bias),
+        conv_states.ctypes.data, conv_states.shape[0], conv_states.strides[0] // 2,
+        conv_states.strides[1] // 2, conv_states.strides[2] // 2,
+        cache_indices.ctypes.data, cache_indices.strides[0] // 4,
+        part_dim, int(is_silu(activation)), int(null_block_id is not None),
+        0 if null_block_id is None else int(null_block_id), out.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle rejected the call (bad shapes)")
+    return out
 
 
 def run_workload(wl, out: Optional[np.ndarray] = None, lib=None):

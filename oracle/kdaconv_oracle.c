@@ -22,6 +22,10 @@
  *     the weights are FP32, and the output has x's dtype (the function's
  *     docstring); the arithmetic is FP32 for every input dtype (the note after
  *     the module docstring: the stock kernel computes in the state dtype).
+ * and, for the decode step with a bf16 state, from the page
+ * "vllm.models.kimi_k3.amd.ops.kda_decode": is_fused_kda_decode_supported (bf16
+ * input, bf16 conv state) and make_decode_conv1d_weight_loader (the FP32 weight
+ * mirrored width-major); its readings are stated at the function.
  *
  * Readings taken where the page is silent (each is listed in the design doc):
  *   - tap 3 multiplies the current token, tap 0 the token three back (causal
@@ -332,6 +336,61 @@ int oracle_packed_causal_conv1d(
       if (live)
         for (int k = 0; k < 3; ++k)
           conv_states[line * cs_stride0 + c * cs_stride1 + k * cs_stride2] = hist[k];
+    }
+  }
+  return ORACLE_OK;
+}
+
+/* The decode step with the operands of the fused decode kernel on page
+ * "vllm.models.kimi_k3.amd.ops.kda_decode": bf16 x with a bf16 conv state (the
+ * dtypes is_fused_kda_decode_supported admits) and the FP32 weight mirrored
+ * width-major, [part][width][channel within the part] (the docstring of
+ * make_decode_conv1d_weight_loader). Row b of x is the one token of sequence b;
+ * its history is the sequence's stored line.
+ *
+ * weight:      FP32, tap k of channel c at weight[(c / part_dim) * w_part_stride +
+ *              (c % part_dim) * w_stride0 + k * w_stride1] (width-major:
+ *              w_part_stride = 4 * part_dim, w_stride0 = 1, w_stride1 = part_dim).
+ * conv_states: bf16 words, history k of channel c of line l at
+ *              conv_states[l * cs_stride0 + c * cs_stride1 + k * cs_stride2].
+ * Everything else as in oracle_packed_causal_conv1d, with one token per sequence
+ * and every initial-state flag set.
+ *
+ * Readings (the page prints the dtypes and the weight layout, not the arithmetic):
+ *   - the arithmetic is the FP32 chain of the prefill page: the weight is FP32 and
+ *     bf16 values widen exactly, so the history and the token enter the chain as
+ *     FP32 values and the output is rounded as for the FP32 state;
+ *   - the line then holds entries 1 and 2 and the token. These are bf16 values
+ *     already, so the words are kept as they are (a NaN keeps its payload); no
+ *     rounding takes place. */
+int oracle_packed_causal_conv1d_update_bf16_state(
+    const uint16_t* x, int64_t batch, int64_t dim, int64_t x_row_stride,
+    const float* weight, int64_t w_part_stride, int64_t w_stride0, int64_t w_stride1,
+    const float* bias, uint16_t* conv_states, int64_t num_cache_lines, int64_t cs_stride0,
+    int64_t cs_stride1, int64_t cs_stride2, const int32_t* cache_indices, int64_t ci_stride,
+    int64_t part_dim, int silu, int has_null_block, int64_t null_block_id, uint16_t* out) {
+  if (batch < 0 || dim < 0 || part_dim <= 0 || dim % part_dim != 0 || x_row_stride < dim)
+    return ORACLE_EINVAL;
+  for (int64_t b = 0; b < batch; ++b) {
+    int64_t line = cache_indices[b * ci_stride];
+    int live = line >= 0 && line < num_cache_lines && !(has_null_block && line == null_block_id);
+    for (int64_t c = 0; c < dim; ++c) {
+      uint16_t words[3] = {0, 0, 0}; /* +0.0 history when there is no line */
+      if (live)
+        for (int k = 0; k < 3; ++k)
+          words[k] = conv_states[line * cs_stride0 + c * cs_stride1 + k * cs_stride2];
+      float hist[3];
+      for (int k = 0; k < 3; ++k) hist[k] = oracle_bf16_to_f32(words[k]);
+      uint16_t xw = x[b * x_row_stride + c];
+      int64_t plane = c / part_dim, col = c % part_dim;
+      const float* w = weight + plane * w_part_stride + col * w_stride0;
+      float acc = conv_acc(w, w_stride1, bias ? bias + c : NULL, hist, oracle_bf16_to_f32(xw));
+      out[(plane * batch + b) * part_dim + col] = (uint16_t)oracle_act_word(acc, silu, ORACLE_BF16);
+      if (live) {
+        conv_states[line * cs_stride0 + c * cs_stride1 + 0 * cs_stride2] = words[1];
+        conv_states[line * cs_stride0 + c * cs_stride1 + 1 * cs_stride2] = words[2];
+        conv_states[line * cs_stride0 + c * cs_stride1 + 2 * cs_stride2] = xw;
+      }
     }
   }
   return ORACLE_OK;

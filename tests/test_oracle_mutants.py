@@ -12,6 +12,7 @@ import pytest
 import oracle
 import test_oracle_act as act_pins
 import test_oracle_conv as conv_pins
+import test_oracle_decode_bf16_state as bf16_state_pins
 import test_oracle_formats as format_pins
 import test_oracle_rounding as round_pins
 
@@ -65,6 +66,16 @@ MUTANTS = {
     "f32 output NaN payload kept": [("isnan(y) ? 0x7FC00000u : bits_of(y)", "bits_of(y)")],
     "f16 read as bf16": [("return fmt == ORACLE_F16 ? oracle_f16_to_f32(h) : oracle_bf16_to_f32(h);",
                           "return oracle_bf16_to_f32(h);")],
+    "bf16 state: token word rounded through FP32": [
+        ("2 * cs_stride2] = xw;", "2 * cs_stride2] = oracle_f32_to_bf16(oracle_bf16_to_f32(xw));")],
+    "bf16 state: part stride ignored": [("weight + plane * w_part_stride + col * w_stride0",
+                                         "weight + c * w_stride0")],
+    "bf16 state: oldest entry kept": [("0 * cs_stride2] = words[1];", "0 * cs_stride2] = words[0];")],
+    "bf16 state: null block ignored": [
+        ("&& !(has_null_block && line == null_block_id);", ";")],
+    "bf16 state: width and channel strides swapped": [
+        ("col * w_stride0;\n      float acc = conv_acc(w, w_stride1,",
+         "col * w_stride1;\n      float acc = conv_acc(w, w_stride0,")],
     "exp one ulp high": [("    return (float)q;\n  }\n  return (float)e;",
                           "    return (float)q;\n  }\n  return nextafterf((float)e, INFINITY);")],
 }
@@ -94,6 +105,10 @@ PINS = [
     ("f32 word", format_pins.test_f32_word_reading),
     *[(f"brute force {f} {s}", lambda lib, f=f, s=s: format_pins.test_brute_force_exact(lib, f, s))
       for f in ("f16", "f32") for s in range(3)],
+    ("bf16 state brute force", lambda lib: bf16_state_pins.test_brute_force_exact(lib, 0)),
+    ("bf16 state width-major taps", bf16_state_pins.test_width_major_taps_land_on_their_channels),
+    ("bf16 state NaN words", bf16_state_pins.test_nan_words_keep_their_payloads),
+    ("bf16 state null block", lambda lib: bf16_state_pins.test_null_block_and_lines_outside(lib, -1)),
 ]
 
 

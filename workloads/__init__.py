@@ -268,6 +268,75 @@ def decode_batch(batch: int = 256, seed: int = 6, x_dtype: str = "bf16") -> Work
                     np.ones(batch, dtype=bool), 1536, "silu", None, x_dtype)
 
 
+@dataclasses.dataclass
+class Bf16StateDecode:
+    """One decode step with the operands of the fused decode kernel on page
+    vllm.models.kimi_k3.amd.ops.kda_decode: bf16 x, a bf16 conv state and the FP32
+    weight mirrored width-major, ``(dim // part_dim, 4, part_dim)`` [part, width,
+    channel]. Row b of ``x`` (raw bf16 words, ``(batch, row_stride)``) is the one token
+    of sequence b; ``conv_states`` holds raw bf16 words ``(lines, dim, 3)``."""
+
+    name: str
+    x: np.ndarray
+    dim: int
+    weight: np.ndarray  # float32 (parts, 4, part_dim)
+    bias: Optional[np.ndarray]
+    conv_states: np.ndarray  # uint16 (lines, dim, 3)
+    cache_indices: np.ndarray  # int32 (batch,)
+    part_dim: int
+    activation: Optional[str]
+    null_block_id: Optional[int]
+
+    @property
+    def batch(self) -> int:
+        return int(self.x.shape[0])
+
+    @property
+    def num_cache_lines(self) -> int:
+        return int(self.conv_states.shape[0])
+
+    def algorithmic_bytes(self) -> int:
+        """x read and out written (2 B per element each), 6 B of state per channel read
+        and written for every live sequence, the weight (16 B per channel), the bias
+        (4 B per channel) and the cache indices."""
+        ci = self.cache_indices.astype(np.int64)
+        live = (ci >= 0) & (ci < self.num_cache_lines)
+        if self.null_block_id is not None:
+            live &= ci != self.null_block_id
+        b = 4 * self.batch * self.dim + 12 * self.dim * int(live.sum()) + 16 * self.dim
+        if self.bias is not None:
+            b += 4 * self.dim
+        return b + 4 * self.batch
+
+
+def width_major(weight: np.ndarray, part_dim: int) -> np.ndarray:
+    """A (dim, 4) [channel, width] weight rearranged as (dim // part_dim, 4, part_dim)
+    [part, width, channel] (page vllm.models.kimi_k3.amd.ops.kda_decode,
+    make_decode_conv1d_weight_loader: the decode kernel's copy of the weight)."""
+    dim = weight.shape[0]
+    return np.ascontiguousarray(weight.reshape(dim // part_dim, part_dim, 4).transpose(0, 2, 1))
+
+
+def decode_batch_bf16_state(batch: int = 256, seed: int = 8, dim: int = 4608,
+                            part_dim: int = 1536, row_stride: int = IN_PROJ_ROW_STRIDE,
+                            lines: Optional[int] = None,
+                            null_block_id: Optional[int] = None) -> Bf16StateDecode:
+    """A decode step of ``batch`` sequences with the decode kernel's operands: dim 4608
+    = 3 x 1536 bf16 x in rows of 9728, bias, SiLU, a bf16 state of max(1024, batch)
+    lines drawn N(0, 1) and rounded to bf16, distinct random lines."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    lines = lines or max(1024, batch)
+    x = _x_buffer(rng, batch, dim, row_stride)
+    w = _normal(rng, (dim, 4), 0.5)
+    b = _normal(rng, (dim,), 0.1)
+    st = f32_to_bf16_bits(_normal(rng, (lines, dim, 3), 1.0))
+    ci = rng.permutation(lines)[:batch].astype(np.int32)
+    return Bf16StateDecode(f"decode, bf16 state: {batch} sequences x 1 token, dim {dim}, "
+                           f"part_dim {part_dim}, stride {row_stride}",
+                           x, dim, width_major(w, part_dim), b, st, ci, part_dim, "silu",
+                           null_block_id)
+
+
 def large_output_case(seed: int = 7) -> Workload:
     """An output of 2.4 GB, beyond the 2 GiB a single launch addresses: 262144 tokens,
     dim 4608 = 3 x 1536 contiguous (x is 2.4 GB as well), six sequences including lengths
