@@ -177,31 +177,42 @@ def fmt_label(x_dtype: str) -> str:
 def time_config(kd, torch, wl, steps: int, warmup: int, blocks: int = 10, decode: bool = False,
                 settle_ms: float = 30.0):
     """Back-to-back per-launch times of the conv (or, with decode, of the decode step) on
-    one workload, with complete input/output/state sets rotated past the Infinity Cache."""
+    one workload, with complete input/output/state sets rotated past the Infinity Cache.
+    A ``workloads.Bf16StateDecode`` is timed as the decode step with its bf16 state and
+    width-major weight."""
     dev = torch.device("cuda:0")
+    bf16_state = not hasattr(wl, "query_start_loc")
+    tokens = wl.batch if bf16_state else wl.num_tokens
+    x_dtype = "bf16" if bf16_state else wl.x_dtype
     P = wl.dim // wl.part_dim
-    xb = x_tensor(torch, wl, dev)
+    if bf16_state:
+        xb = torch.from_numpy(wl.x.view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        xb = x_tensor(torch, wl, dev)
     eb = xb.element_size()
-    set_bytes = wl.x.nbytes + P * wl.num_tokens * wl.part_dim * eb + wl.conv_states.nbytes
+    set_bytes = wl.x.nbytes + P * tokens * wl.part_dim * eb + wl.conv_states.nbytes
     sets = rotation_sets(set_bytes)
     bufs = []
     for i in range(sets):
         x = xb.clone() if i else xb
+        st = torch.from_numpy(wl.conv_states.copy().view(np.int16) if bf16_state
+                              else wl.conv_states.copy()).to(dev)
         bufs.append(dict(
             x=x[:, : wl.dim],
-            st=torch.from_numpy(wl.conv_states.copy()).to(dev),
-            out=torch.empty((P, wl.num_tokens, wl.part_dim), dtype=xb.dtype, device=dev),
+            st=st.view(torch.bfloat16) if bf16_state else st,
+            out=torch.empty((P, tokens, wl.part_dim), dtype=xb.dtype, device=dev),
         ))
     w = torch.from_numpy(wl.weight).to(dev)
     b = None if wl.bias is None else torch.from_numpy(wl.bias).to(dev)
-    q = torch.from_numpy(wl.query_start_loc).to(dev)
     ci = torch.from_numpy(wl.cache_indices).to(dev)
-    init = torch.from_numpy(wl.has_initial_state).to(dev)
+    if not bf16_state:
+        q = torch.from_numpy(wl.query_start_loc).to(dev)
+        init = torch.from_numpy(wl.has_initial_state).to(dev)
     stream = torch.cuda.current_stream(dev)
 
     def step(i):
         s = bufs[i % sets]
-        if decode:
+        if decode or bf16_state:
             kd.packed_causal_conv1d_update(s["x"], w, b, s["st"], ci, wl.part_dim, wl.activation,
                                            wl.null_block_id, out=s["out"])
         else:
@@ -212,7 +223,7 @@ def time_config(kd, torch, wl, steps: int, warmup: int, blocks: int = 10, decode
     for i in range(warmup):
         step(n + i)
     us = back_to_back(torch, stream, step, steps, blocks)
-    res = {"workload": wl.name + f", x and out {fmt_label(wl.x_dtype)}", "buffer_sets_rotated": sets}
+    res = {"workload": wl.name + f", x and out {fmt_label(x_dtype)}", "buffer_sets_rotated": sets}
     res.update(summary(wl.algorithmic_bytes(), us))
     del bufs
     torch.cuda.empty_cache()
@@ -538,6 +549,12 @@ def main() -> int:
             str(bsz): time_config(kd, torch, workloads.decode_batch(bsz), steps=20, warmup=5,
                                   decode=True)
             for bsz in (64, 256, 1024, 4096)
+        }
+        # Decode steps with the decode kernel page's operands: bf16 state, width-major weight.
+        result["decode_bf16_state"] = {
+            str(bsz): time_config(kd, torch, workloads.decode_batch_bf16_state(bsz), steps=20,
+                                  warmup=5)
+            for bsz in (1024, 4096)
         }
         # The same 16K-token workload with fp16 and FP32 x (output in x's format).
         result["other_formats"] = {

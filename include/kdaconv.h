@@ -140,7 +140,8 @@ int kdaconv_packed_causal_conv1d(
  * activated, rounded tap sum, and the line becomes entries 1, 2 and the new token.
  * With an FP32 state the arithmetic is FP32 for every x dtype (page
  * "vllm.models.kimi_k3.nvidia.ops.kda_conv", packed_causal_conv1d_supported's note).
- * The bf16 state of that page's decode kernel is not supported.
+ * The bf16 state of the decode page's kernel is taken by
+ * kdaconv_packed_causal_conv1d_update_bf16_state below.
  *
  * x                  elements of format dtype, (batch, dim) at row stride
  *                    x_row_stride (16-byte aligned rows, as for the prefill op).
@@ -165,6 +166,53 @@ int kdaconv_packed_causal_conv1d_update(
     const float* weight, int64_t weight_stride0, int64_t weight_stride1,
     const float* bias,
     float* conv_states, int64_t num_cache_lines,
+    int64_t cs_stride0, int64_t cs_stride1, int64_t cs_stride2,
+    const int32_t* cache_indices, int64_t cache_indices_stride,
+    int64_t part_dim, int activation, int has_null_block, int64_t null_block_id,
+    void* out, kdaconv_stream_t stream);
+
+/*
+ * The decode step with the operands of the fused decode kernel on page
+ * "vllm.models.kimi_k3.amd.ops.kda_decode": a bf16 conv state and the FP32 weight
+ * mirrored width-major (is_fused_kda_decode_supported admits a bf16 input with a bf16
+ * conv state, not dim-first; make_decode_conv1d_weight_loader's docstring gives the
+ * weight as [qkv, width, channel]). The page prints no arithmetic. The reading taken:
+ * the state's bf16 values and the token widen exactly to FP32 and go through the same
+ * FP32 chain, activation and rounding as kdaconv_packed_causal_conv1d_update, so the
+ * output equals that call on the widened state; the line then holds entries 1 and 2
+ * and the token, whose words are kept unchanged (they are bf16 values already; a NaN
+ * keeps its payload).
+ *
+ * x                  bf16 (batch, dim) at row stride x_row_stride (16-byte aligned
+ *                    rows). dtype must be KDACONV_BF16 (the page's gate); fp16 and
+ *                    FP32 give EUNSUPPORTED, unknown codes EINVAL.
+ * weight             FP32; tap k of channel c at weight[(c / part_dim) *
+ *                    weight_part_stride + (c % part_dim) * weight_stride0 + k *
+ *                    weight_stride1]. The page's width-major (dim / part_dim, 4,
+ *                    part_dim) array is part stride 4 * part_dim, stride0 1, stride1
+ *                    part_dim, and the prefill op's (dim, 4) array is 4 * part_dim,
+ *                    4, 1; both take vector paths when 16-byte aligned, any other
+ *                    strides a scalar one.
+ * conv_states        bf16 words, logical shape (num_cache_lines, dim, 3): history k
+ *                    of channel c of line l at conv_states[l * cs_stride0 + c *
+ *                    cs_stride1 + k * cs_stride2]; (lines, dim, 3) contiguous and
+ *                    8-byte aligned takes a vector path, any other strides a scalar
+ *                    one. Read and written in place.
+ * bias, cache_indices,
+ * part_dim, activation,
+ * has_null_block,
+ * null_block_id, out as for kdaconv_packed_causal_conv1d_update (out is bf16).
+ *
+ * Precondition (not checked): live lines distinct within the batch.
+ * batch == 0 or dim == 0 returns KDACONV_OK with no launch. Status codes and their
+ * checks are those of kdaconv_packed_causal_conv1d_update, and a negative
+ * weight_part_stride gives EUNSUPPORTED.
+ */
+int kdaconv_packed_causal_conv1d_update_bf16_state(
+    const void* x, int dtype, int64_t batch, int64_t dim, int64_t x_row_stride,
+    const float* weight, int64_t weight_part_stride, int64_t weight_stride0,
+    int64_t weight_stride1, const float* bias,
+    uint16_t* conv_states, int64_t num_cache_lines,
     int64_t cs_stride0, int64_t cs_stride1, int64_t cs_stride2,
     const int32_t* cache_indices, int64_t cache_indices_stride,
     int64_t part_dim, int activation, int has_null_block, int64_t null_block_id,

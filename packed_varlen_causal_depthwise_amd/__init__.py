@@ -169,6 +169,40 @@ def packed_causal_conv1d_fn(
     return out
 
 
+def _check_bf16_state(x, weight, bias, conv_states, cache_indices, batch, part_dim):
+    if x.dtype != torch.bfloat16:
+        raise ValueError("a bf16 conv state takes bf16 x (page: is_fused_kda_decode_supported)")
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D (batch, dim) with unit column stride")
+    dim = x.size(1)
+    parts = dim // part_dim
+    if weight.dtype != torch.float32 or not (
+            (weight.dim() == 2 and tuple(weight.shape) == (dim, 4))
+            or (weight.dim() == 3 and tuple(weight.shape) == (parts, 4, part_dim))):
+        raise ValueError("weight must be float32 (dim, 4) or width-major "
+                         "(dim // part_dim, 4, part_dim)")
+    if bias is not None and (bias.dtype != torch.float32 or tuple(bias.shape) != (dim,)
+                             or not bias.is_contiguous()):
+        raise ValueError("bias must be a contiguous float32 (dim,) tensor or None")
+    if conv_states.dim() != 3 or conv_states.size(1) != dim or conv_states.size(2) < 3:
+        raise ValueError("conv_states must be bf16 of shape (cache lines, dim, >= 3)")
+    if cache_indices.dtype != torch.int32 or cache_indices.dim() != 1 or cache_indices.numel() < batch:
+        raise ValueError("cache_indices must be a 1-D int32 tensor with one entry per sequence")
+    if not x.is_cuda:
+        raise ValueError("x must be a GPU tensor")
+    for t in (weight, bias, conv_states, cache_indices):
+        if t is not None and t.device != x.device:
+            raise ValueError("all tensors must be on the device of x")
+
+
+def _weight_strides(weight: torch.Tensor, part_dim: int):
+    """(part stride, channel stride, width stride) of a (dim, 4) or a width-major
+    (dim // part_dim, 4, part_dim) weight, in elements."""
+    if weight.dim() == 2:
+        return part_dim * weight.stride(0), weight.stride(0), weight.stride(1)
+    return weight.stride(0), weight.stride(2), weight.stride(1)
+
+
 def packed_causal_conv1d_update(
     x: torch.Tensor,
     weight: torch.Tensor,
@@ -182,12 +216,17 @@ def packed_causal_conv1d_update(
 ) -> torch.Tensor:
     """Decode step: one token per sequence, row b of x (batch, dim) for sequence b.
 
-    The packed causal conv1d update of page vllm.models.kimi_k3.amd.ops.kda_decode
-    with the FP32 state of packed_causal_conv1d_fn: the result equals that function
-    with query_start_loc = [0, 1, ..., batch] and every has_initial_state true. The
-    state lines named by cache_indices shift by one token in place (the null
-    block's line is neither read nor written). Returns (dim // part_dim, batch,
-    part_dim) in x's dtype. Queued on the current stream; no synchronisation.
+    The packed causal conv1d update of page vllm.models.kimi_k3.amd.ops.kda_decode.
+    With a float32 conv_states (the state of packed_causal_conv1d_fn) the result equals
+    that function with query_start_loc = [0, 1, ..., batch] and every has_initial_state
+    true, for bf16, fp16 or float32 x. With a bfloat16 conv_states (the decode page's
+    fused kernel state) x must be bf16 and the weight may also be that page's
+    width-major (dim // part_dim, 4, part_dim) float32 copy; the arithmetic is the same
+    FP32 chain on the exactly widened state, and the line keeps the words of its
+    entries 1, 2 and the token. The state lines named by cache_indices shift by one
+    token in place (the null block's line is neither read nor written). Returns
+    (dim // part_dim, batch, part_dim) in x's dtype. Queued on the current stream; no
+    synchronisation.
     """
     if x.dim() != 2:
         raise ValueError("x must be 2-D (batch, dim)")
@@ -201,18 +240,27 @@ def packed_causal_conv1d_update(
         raise ValueError(f"out must be a contiguous {x.dtype} tensor of shape {shape} on {x.device}")
     if batch == 0:
         return out
-    _check_common(x, weight, bias, conv_states, cache_indices, batch)
+    bf16_state = conv_states.dtype == torch.bfloat16
+    if bf16_state:
+        _check_bf16_state(x, weight, bias, conv_states, cache_indices, batch, part_dim)
+    else:
+        _check_common(x, weight, bias, conv_states, cache_indices, batch)
     lib = _lib.load()
-    with torch.cuda.device(x.device):
-        rc = lib.kdaconv_packed_causal_conv1d_update(
-            _ptr(x), _dtype_code(x.dtype), batch, dim, x.stride(0),
-            _ptr(weight), weight.stride(0), weight.stride(1), _ptr(bias),
-            _ptr(conv_states), conv_states.size(0),
-            conv_states.stride(0), conv_states.stride(1), conv_states.stride(2),
-            _ptr(cache_indices), cache_indices.stride(0),
+    tail = (_ptr(cache_indices), cache_indices.stride(0),
             int(part_dim), _activation_code(activation),
             int(null_block_id is not None), 0 if null_block_id is None else int(null_block_id),
             _ptr(out), _stream_handle(x.device))
+    states = (_ptr(conv_states), conv_states.size(0),
+              conv_states.stride(0), conv_states.stride(1), conv_states.stride(2))
+    with torch.cuda.device(x.device):
+        if bf16_state:
+            rc = lib.kdaconv_packed_causal_conv1d_update_bf16_state(
+                _ptr(x), _dtype_code(x.dtype), batch, dim, x.stride(0),
+                _ptr(weight), *_weight_strides(weight, part_dim), _ptr(bias), *states, *tail)
+        else:
+            rc = lib.kdaconv_packed_causal_conv1d_update(
+                _ptr(x), _dtype_code(x.dtype), batch, dim, x.stride(0),
+                _ptr(weight), weight.stride(0), weight.stride(1), _ptr(bias), *states, *tail)
     _lib.check(rc, "packed_causal_conv1d_update")
     return out
 

@@ -15,6 +15,7 @@ BF16, F16, F32 = 0, 1, 2
 EXPORTS = (
     "kdaconv_packed_causal_conv1d",
     "kdaconv_packed_causal_conv1d_update",
+    "kdaconv_packed_causal_conv1d_update_bf16_state",
     "kdaconv_validate",
     "kdaconv_activation_map",
     "kdaconv_status_string",
@@ -59,6 +60,15 @@ def load() -> ctypes.CDLL:
         vp, vp,  # out, stream
     ]
     lib.kdaconv_packed_causal_conv1d_update.restype = i32
+    lib.kdaconv_packed_causal_conv1d_update_bf16_state.argtypes = [
+        vp, i32, i64, i64, i64,  # x, dtype, batch, dim, x_row_stride
+        vp, i64, i64, i64, vp,  # weight, part stride, channel stride, width stride, bias
+        vp, i64, i64, i64, i64,  # conv_states (bf16), num_cache_lines, strides
+        vp, i64,  # cache_indices, stride
+        i64, i32, i32, i64,  # part_dim, activation, has_null_block, null_block_id
+        vp, vp,  # out, stream
+    ]
+    lib.kdaconv_packed_causal_conv1d_update_bf16_state.restype = i32
     lib.kdaconv_validate.argtypes = conv_args
     lib.kdaconv_validate.restype = i32
     lib.kdaconv_activation_map.argtypes = [ctypes.c_uint32, i64, i32, i32, vp, vp]

@@ -70,6 +70,10 @@ constexpr int kStream = 2;  // nontemporal
 constexpr int kKeep = 0;  // default caching
 constexpr uint32_t kDescWord3 = 0x00020000u;  // gfx9 raw buffer: 32-bit data format
 constexpr int32_t kRange = 0x7FFFFFFF;
+// Conv-state element formats: the FP32 state of the prefill op, and the bf16 state
+// of the decode step with the fused decode kernel's operands.
+constexpr int kStateF32 = 0;
+constexpr int kStateBF16 = 1;
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -125,6 +129,8 @@ struct ConvParams {
   char* out;  // first plane of this launch
   int64_t x_row_stride;
   int64_t w_stride0, w_stride1;
+  int64_t w_part_stride;  // tap k of channel c at (c / part_dim) * w_part_stride +
+                          // (c % part_dim) * w_stride0 + k * w_stride1
   int64_t cs_stride0, cs_stride1, cs_stride2;
   int64_t ci_stride;
   int64_t num_cache_lines;
@@ -152,8 +158,11 @@ struct ConvParams {
   int32_t search_top;  // 64^(search_levels - 1)
   int32_t has_null_block;
   int32_t weight_vec;  // weight is (dim, 4) contiguous and 16-byte aligned
+  int32_t weight_wm;  // bf16-state decode: weight is width-major with 4-aligned strides,
+                      // 16-byte aligned (a lane's 4 channels of one tap are one vector)
   int32_t bias_vec;  // bias is 16-byte aligned
   int32_t state_vec;  // each state line is (dim, 3) contiguous and 16-byte aligned
+                      // (bf16 state: 8-byte aligned)
   int32_t state_rows;  // each state line is 3 rows of dim contiguous channels ("dim first"),
                        // 16-byte aligned, row and line strides multiples of 4
 };
@@ -379,7 +388,7 @@ __device__ __forceinline__ Tile describe_tile(const ConvParams& P, int p, int la
 // The per-wave part of the convolution shared by the prefill and decode kernels:
 // the lane's channels, its weights and bias, the state line's I/O, prefill tiles
 // and decode steps.
-template <int kF, int V, int R, bool kBias, bool kSilu>
+template <int kF, int V, int R, bool kBias, bool kSilu, int kS = kStateF32>
 struct ConvWorker {
   static constexpr int kBytes = element_bytes<kF>();
   typedef Lane<V * kBytes> L;
@@ -417,7 +426,40 @@ struct ConvWorker {
   // rows: vector memory operations complete in issue order, so loads issued after
   // the rows could only be used once all the rows had arrived.
   __device__ __forceinline__ void load_weights() {
-    if (P.weight_vec) {
+    if (kS == kStateBF16 && P.weight_wm) {
+      // Width-major: tap k of the lane's V channels (one plane, consecutive columns)
+      // is V consecutive floats.
+      const __amdgpu_buffer_rsrc_t wr = make_rsrc(P.weight);
+      const int plane = cl / P.part_dim;
+      const uint32_t base = (uint32_t)(plane * P.w_part_stride + (cl - plane * P.part_dim));
+#pragma unroll
+      for (int i = 0; i < V / 4; ++i) {
+        const uint32_t o = (base + 4u * i) * 4u;
+        const u32x4 t0 = __builtin_amdgcn_raw_buffer_load_b128(wr, o, 0, kKeep);
+        const u32x4 t1 = __builtin_amdgcn_raw_buffer_load_b128(wr, o + (uint32_t)P.w_stride1 * 4u, 0, kKeep);
+        const u32x4 t2 = __builtin_amdgcn_raw_buffer_load_b128(wr, o + (uint32_t)P.w_stride1 * 8u, 0, kKeep);
+        const u32x4 t3 = __builtin_amdgcn_raw_buffer_load_b128(wr, o + (uint32_t)P.w_stride1 * 12u, 0, kKeep);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          w0[4 * i + k] = __uint_as_float(t0[k]);
+          w1[4 * i + k] = __uint_as_float(t1[k]);
+          w2[4 * i + k] = __uint_as_float(t2[k]);
+          w3[4 * i + k] = __uint_as_float(t3[k]);
+        }
+      }
+    } else if (kS == kStateBF16 && !P.weight_vec) {
+      // Any strides, with the part stride; the lane's channels lie in one plane.
+      const int plane = cl / P.part_dim;
+      const float* base = P.weight + plane * P.w_part_stride;
+#pragma unroll
+      for (int k = 0; k < V; ++k) {
+        const float* wp = base + (int64_t)(cl + k - plane * P.part_dim) * P.w_stride0;
+        w0[k] = wp[0];
+        w1[k] = wp[P.w_stride1];
+        w2[k] = wp[2 * P.w_stride1];
+        w3[k] = wp[3 * P.w_stride1];
+      }
+    } else if (P.weight_vec) {
       const __amdgpu_buffer_rsrc_t wr = make_rsrc(P.weight);
 #pragma unroll
       for (int k = 0; k < V; ++k) {
@@ -588,6 +630,102 @@ struct ConvWorker {
       __builtin_amdgcn_raw_buffer_store_b128(s4[lane + kWave * q], r, (uint32_t)(lane + kWave * q) * 16u, 0, kKeep);
   }
 
+  // bf16 state lines. Values widen exactly (the word in the upper half of the FP32
+  // word) and go back by taking that half again, so entries and tokens are stored
+  // with their words unchanged.
+  __device__ __forceinline__ static float widen_bf16(uint32_t word16) {
+    return __uint_as_float(word16 << 16);
+  }
+  __device__ __forceinline__ static uint32_t bf16_word(float v) { return __float_as_uint(v) >> 16; }
+
+  // The lane's V channels of bf16 state line `line`: h0, h1, h2 = entries 0, 1, 2.
+  __device__ __forceinline__ void load_state16(int64_t line, float (&h0)[V], float (&h1)[V],
+                                               float (&h2)[V]) const {
+    const uint16_t* sp = reinterpret_cast<const uint16_t*>(P.states) + line * P.cs_stride0;
+    if (P.state_vec) {
+      // The lane's V channels x 3 entries are 3V consecutive words, 8-byte aligned.
+      const __amdgpu_buffer_rsrc_t sr = make_rsrc(sp);
+      uint32_t d[3 * V / 2];
+#pragma unroll
+      for (int i = 0; i < 3 * V / 4; ++i) {
+        const u32x2 t = __builtin_amdgcn_raw_buffer_load_b64(sr, (uint32_t)cl * 6u + 8u * i, 0, kKeep);
+        d[2 * i] = t[0];
+        d[2 * i + 1] = t[1];
+      }
+#pragma unroll
+      for (int k = 0; k < V; ++k) {
+        uint32_t e[3];
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+          const int idx = 3 * k + j;
+          e[j] = (d[idx / 2] >> (16 * (idx % 2))) & 0xFFFFu;
+        }
+        h0[k] = widen_bf16(e[0]);
+        h1[k] = widen_bf16(e[1]);
+        h2[k] = widen_bf16(e[2]);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < V; ++k) {
+        const uint16_t* cp = sp + (int64_t)(cl + k) * P.cs_stride1;
+        h0[k] = widen_bf16(cp[0]);
+        h1[k] = widen_bf16(cp[P.cs_stride2]);
+        h2[k] = widen_bf16(cp[2 * P.cs_stride2]);
+      }
+    }
+  }
+
+  // Writes entries 0, 1, 2 of the lane's V channels of bf16 line `line`, any strides
+  // (active lanes only).
+  __device__ __forceinline__ void store_state16(int64_t line, const float (&h0)[V],
+                                                const float (&h1)[V], const float (&h2)[V]) const {
+    uint16_t* sp = reinterpret_cast<uint16_t*>(P.states) + line * P.cs_stride0;
+#pragma unroll
+    for (int k = 0; k < V; ++k) {
+      uint16_t* cp = sp + (int64_t)(cl + k) * P.cs_stride1;
+      cp[0] = (uint16_t)bf16_word(h0[k]);
+      cp[P.cs_stride2] = (uint16_t)bf16_word(h1[k]);
+      cp[2 * P.cs_stride2] = (uint16_t)bf16_word(h2[k]);
+    }
+  }
+
+  // Staged write of a contiguous (dim, 3) bf16 line, as store_state_staged does for
+  // FP32 lines: the wave's channels [cfirst, cfirst + n) are 6 n consecutive bytes and
+  // lane l's V channels bytes [6 V l, 6 V (l + 1)). Lanes write their 6 V bytes to the
+  // slice at their slot; then each of 3 V / 4 store instructions takes 64 consecutive
+  // 8-byte pieces (512 bytes). 6 n is a multiple of 8 (n is a multiple of 4), so no
+  // piece straddles the end of the part, and pieces at or past it (read from bytes of
+  // the slice no lane wrote) are dropped by the descriptor's range.
+  __device__ __forceinline__ void store_state16_staged(int64_t line, const float (&h0)[V],
+                                                       const float (&h1)[V],
+                                                       const float (&h2)[V]) const {
+    constexpr int kPieces = 3 * V / 4;  // 8-byte pieces per lane
+    u32x2* s2 = reinterpret_cast<u32x2*>(stage);
+    const int slot = (cl - cfirst) / V;
+    uint32_t e[3 * V];
+#pragma unroll
+    for (int k = 0; k < V; ++k) {
+      e[3 * k] = bf16_word(h0[k]);
+      e[3 * k + 1] = bf16_word(h1[k]);
+      e[3 * k + 2] = bf16_word(h2[k]);
+    }
+    slice_fence();  // earlier reads of the slice are done
+#pragma unroll
+    for (int q = 0; q < kPieces; ++q) {
+      u32x2 t;
+      t[0] = e[4 * q] | (e[4 * q + 1] << 16);
+      t[1] = e[4 * q + 2] | (e[4 * q + 3] << 16);
+      s2[kPieces * slot + q] = t;
+    }
+    slice_fence();
+    const int n = min(kWave * V, P.col_end - cfirst);
+    uint16_t* sp = reinterpret_cast<uint16_t*>(P.states) + line * P.cs_stride0 + (int64_t)cfirst * 3;
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(sp, (short)0, n * 6, kDescWord3);
+#pragma unroll
+    for (int q = 0; q < kPieces; ++q)
+      __builtin_amdgcn_raw_buffer_store_b64(s2[lane + kWave * q], r, (uint32_t)(lane + kWave * q) * 8u, 0, kKeep);
+  }
+
   // Decode steps of sequences s0 .. s0 + kSeq - 1 (those below num_seqs): all their
   // loads (cache lines, x rows, state lines) are issued before any arithmetic, then
   // each sequence is computed and stored in turn.
@@ -613,7 +751,10 @@ struct ConvWorker {
 #pragma unroll
     for (int i = 0; i < kSeq; ++i) {
       if (live[i]) {
-        load_state(line[i], h0[i], h1[i], h2[i]);
+        if (kS == kStateBF16)
+          load_state16(line[i], h0[i], h1[i], h2[i]);
+        else
+          load_state(line[i], h0[i], h1[i], h2[i]);
       } else {
 #pragma unroll
         for (int k = 0; k < V; ++k) h0[i][k] = h1[i][k] = h2[i][k] = 0.0f;
@@ -658,10 +799,16 @@ struct ConvWorker {
 #pragma unroll
       for (int w = 0; w < kWords; ++w) o[w] = words[0][w];
       L::template store<kStream>(o, orsrc, ovo, (uint32_t)s * orow_bytes);
-      if (kStaged && live[i])
+      if (kS == kStateBF16) {
+        if (kStaged && live[i])
+          store_state16_staged(line[i], h1[i], h2[i], xv);
+        else if (live[i] && active)
+          store_state16(line[i], h1[i], h2[i], xv);
+      } else if (kStaged && live[i]) {
         store_state_staged(line[i], h1[i], h2[i], xv);
-      else if (live[i] && active)
+      } else if (live[i] && active) {
         store_state(line[i], h1[i], h2[i], xv);
+      }
     }
   }
 
@@ -929,7 +1076,7 @@ __global__ __launch_bounds__(kWave * kG) __attribute__((amdgpu_waves_per_eu(kMin
 // Decode update: program p is sequences kSeq p .. kSeq p + kSeq - 1 (rows of x), one
 // wave per column block, kG column blocks per workgroup. No search: every sequence
 // has exactly one token.
-template <int kF, int V, int kSeq, int kG, bool kBias, bool kSilu>
+template <int kF, int V, int kSeq, int kG, bool kBias, bool kSilu, int kS>
 __global__ __launch_bounds__(kWave * kG) void packed_conv_update_kernel(const ConvParams P) {
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
@@ -938,7 +1085,7 @@ __global__ __launch_bounds__(kWave * kG) void packed_conv_update_kernel(const Co
   const int cb = slot.cb;
   if (cb >= P.col_blocks) return;
   __shared__ float stage[kG][3 * V * kWave];
-  ConvWorker<kF, V, 1, kBias, kSilu> w(P, lane, cb, nullptr, stage[wave]);
+  ConvWorker<kF, V, 1, kBias, kSilu, kS> w(P, lane, cb, nullptr, stage[wave]);
   w.load_weights();
   if (P.state_vec)
     w.template decode_many<kSeq, true>(p * kSeq);
@@ -993,6 +1140,7 @@ __global__ __launch_bounds__(kWave) void activation_map_kernel(uint32_t first, u
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned8(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
 
 bool known_dtype(int dtype) { return dtype == kBF16 || dtype == kF16 || dtype == kF32; }
 
@@ -1025,6 +1173,33 @@ int validate(const void* x, int dtype, int64_t num_tokens, int64_t dim, int64_t 
   if (dim * cs1 * 4 > INT32_MAX) return KDACONV_EUNSUPPORTED;
   if (num_tokens == 0 || num_seqs == 0 || dim == 0) return KDACONV_OK;
   if (!x || !weight || !conv_states || !qsl || !ci || !out) return KDACONV_EINVAL;
+  if (!aligned16(x) || !aligned16(out)) return KDACONV_EUNSUPPORTED;
+  return KDACONV_OK;
+}
+
+// Host checks of the decode step's arguments, for either state format (state_bytes
+// per state element); the weight part stride is checked by the bf16-state entry.
+int validate_update(const void* x, int dtype, int64_t batch, int64_t dim, int64_t x_row_stride,
+                    const float* weight, int64_t ws0, int64_t ws1, int64_t wps,
+                    const void* conv_states, int64_t state_bytes, int64_t num_cache_lines,
+                    int64_t cs0, int64_t cs1, int64_t cs2, const int32_t* cache_indices,
+                    int64_t ci_stride, int64_t part_dim, int activation, const void* out) {
+  if (batch < 0 || dim < 0 || num_cache_lines < 0) return KDACONV_EINVAL;
+  if (!known_dtype(dtype)) return KDACONV_EINVAL;
+  if (part_dim <= 0 || dim % part_dim != 0) return KDACONV_EINVAL;
+  if (x_row_stride < dim) return KDACONV_EINVAL;
+  if (activation != KDACONV_ACT_NONE && activation != KDACONV_ACT_SILU) return KDACONV_EINVAL;
+  const int64_t eb = dtype_bytes(dtype);
+  if (part_dim % 8 != 0 || (x_row_stride * eb) % 16 != 0) return KDACONV_EUNSUPPORTED;
+  if (ws0 < 0 || ws1 < 0 || wps < 0 || cs0 < 0 || cs1 < 0 || cs2 < 0 || ci_stride < 0)
+    return KDACONV_EUNSUPPORTED;
+  if (batch > INT32_MAX - 1 || dim > INT32_MAX / 2) return KDACONV_EUNSUPPORTED;
+  if (batch * ((dim + kWave * kLaneChannels - 1) / (kWave * kLaneChannels)) > INT32_MAX)
+    return KDACONV_EUNSUPPORTED;
+  if (batch * part_dim * eb > INT32_MAX / 2) return KDACONV_EUNSUPPORTED;
+  if (dim * cs1 * state_bytes > INT32_MAX) return KDACONV_EUNSUPPORTED;
+  if (batch == 0 || dim == 0) return KDACONV_OK;
+  if (!x || !weight || !conv_states || !cache_indices || !out) return KDACONV_EINVAL;
   if (!aligned16(x) || !aligned16(out)) return KDACONV_EUNSUPPORTED;
   return KDACONV_OK;
 }
@@ -1072,7 +1247,7 @@ void launch(ConvParams P, int64_t cols, bool bias, bool silu, hipStream_t st) {
     launch_group<kF, V, 1>(P, bias, silu, st);
 }
 
-template <int kF, int V, int kSeq, int kG>
+template <int kF, int V, int kSeq, int kG, int kS>
 void launch_update_group(ConvParams P, bool bias, bool silu, hipStream_t st) {
   const uint64_t groups = ((uint64_t)P.col_blocks + kG - 1) / kG;
   set_wave_order(P, groups, false);
@@ -1080,24 +1255,24 @@ void launch_update_group(ConvParams P, bool bias, bool silu, hipStream_t st) {
   const dim3 block(kWave * kG);
   if (bias) {
     if (silu)
-      hipLaunchKernelGGL((packed_conv_update_kernel<kF, V, kSeq, kG, true, true>), grid, block, 0, st, P);
+      hipLaunchKernelGGL((packed_conv_update_kernel<kF, V, kSeq, kG, true, true, kS>), grid, block, 0, st, P);
     else
-      hipLaunchKernelGGL((packed_conv_update_kernel<kF, V, kSeq, kG, true, false>), grid, block, 0, st, P);
+      hipLaunchKernelGGL((packed_conv_update_kernel<kF, V, kSeq, kG, true, false, kS>), grid, block, 0, st, P);
   } else {
     if (silu)
-      hipLaunchKernelGGL((packed_conv_update_kernel<kF, V, kSeq, kG, false, true>), grid, block, 0, st, P);
+      hipLaunchKernelGGL((packed_conv_update_kernel<kF, V, kSeq, kG, false, true, kS>), grid, block, 0, st, P);
     else
-      hipLaunchKernelGGL((packed_conv_update_kernel<kF, V, kSeq, kG, false, false>), grid, block, 0, st, P);
+      hipLaunchKernelGGL((packed_conv_update_kernel<kF, V, kSeq, kG, false, false, kS>), grid, block, 0, st, P);
   }
 }
 
-template <int kF, int V, int kSeq>
+template <int kF, int V, int kSeq, int kS>
 void launch_update_seq(ConvParams P, bool bias, bool silu, hipStream_t st) {
   P.programs = (P.num_seqs + kSeq - 1) / kSeq;
   if (P.col_blocks % 2 == 0)
-    launch_update_group<kF, V, kSeq, 2>(P, bias, silu, st);
+    launch_update_group<kF, V, kSeq, 2, kS>(P, bias, silu, st);
   else
-    launch_update_group<kF, V, kSeq, 1>(P, bias, silu, st);
+    launch_update_group<kF, V, kSeq, 1, kS>(P, bias, silu, st);
 }
 
 // Sequences per decode wave: as many as keep at least 2048 waves in the launch (two per
@@ -1105,16 +1280,16 @@ void launch_update_seq(ConvParams P, bool bias, bool silu, hipStream_t st) {
 // several sequences per wave instead of one; 256 sequences 12.0 -> 11.8 us with 2; 64
 // sequences unchanged with 1. Eight sequences per wave need about 180 VGPRs, two waves
 // per SIMD: 4096 sequences took 113.6 us with eight and 107.9 us with four.
-template <int kF, int V>
+template <int kF, int V, int kS = kStateF32>
 void launch_update(ConvParams P, int64_t cols, bool bias, bool silu, hipStream_t st) {
   P.col_blocks = (int32_t)((cols / V + kWave - 1) / kWave);
   const int64_t waves1 = (int64_t)P.num_seqs * P.col_blocks;
   if (waves1 >= 4 * 2048)
-    launch_update_seq<kF, V, 4>(P, bias, silu, st);
+    launch_update_seq<kF, V, 4, kS>(P, bias, silu, st);
   else if (waves1 >= 2 * 2048)
-    launch_update_seq<kF, V, 2>(P, bias, silu, st);
+    launch_update_seq<kF, V, 2, kS>(P, bias, silu, st);
   else
-    launch_update_seq<kF, V, 1>(P, bias, silu, st);
+    launch_update_seq<kF, V, 1, kS>(P, bias, silu, st);
 }
 
 // Fields of ConvParams shared by both operations.
@@ -1152,7 +1327,9 @@ void fill_common(ConvParams& P, const void* x, int64_t num_tokens, int64_t x_row
   P.chunk_shift = 0;
   P.full_chunks = 0;
   P.has_null_block = has_null_block != 0;
+  P.w_part_stride = part_dim * ws0;
   P.weight_vec = ws0 == 4 && ws1 == 1 && aligned16(weight);
+  P.weight_wm = 0;
   P.bias_vec = bias != nullptr && aligned16(bias);
   P.state_vec = cs1 == 3 && cs2 == 1 && cs0 % 4 == 0 && aligned16(conv_states);
   P.state_rows = cs1 == 1 && cs2 >= dim && cs2 % 4 == 0 && cs0 % 4 == 0 &&
@@ -1256,24 +1433,12 @@ extern "C" int kdaconv_packed_causal_conv1d_update(
     int64_t cs_stride2, const int32_t* cache_indices, int64_t cache_indices_stride,
     int64_t part_dim, int activation, int has_null_block, int64_t null_block_id, void* out,
     kdaconv_stream_t stream) {
-  if (batch < 0 || dim < 0 || num_cache_lines < 0) return KDACONV_EINVAL;
-  if (!known_dtype(dtype)) return KDACONV_EINVAL;
-  if (part_dim <= 0 || dim % part_dim != 0) return KDACONV_EINVAL;
-  if (x_row_stride < dim) return KDACONV_EINVAL;
-  if (activation != KDACONV_ACT_NONE && activation != KDACONV_ACT_SILU) return KDACONV_EINVAL;
+  const int rc = validate_update(x, dtype, batch, dim, x_row_stride, weight, weight_stride0,
+                                 weight_stride1, 0, conv_states, 4, num_cache_lines, cs_stride0,
+                                 cs_stride1, cs_stride2, cache_indices, cache_indices_stride,
+                                 part_dim, activation, out);
+  if (rc != KDACONV_OK || batch == 0 || dim == 0) return rc;
   const int64_t eb = dtype_bytes(dtype);
-  if (part_dim % 8 != 0 || (x_row_stride * eb) % 16 != 0) return KDACONV_EUNSUPPORTED;
-  if (weight_stride0 < 0 || weight_stride1 < 0 || cs_stride0 < 0 || cs_stride1 < 0 ||
-      cs_stride2 < 0 || cache_indices_stride < 0)
-    return KDACONV_EUNSUPPORTED;
-  if (batch > INT32_MAX - 1 || dim > INT32_MAX / 2) return KDACONV_EUNSUPPORTED;
-  if (batch * ((dim + kWave * kLaneChannels - 1) / (kWave * kLaneChannels)) > INT32_MAX)
-    return KDACONV_EUNSUPPORTED;
-  if (batch * part_dim * eb > INT32_MAX / 2) return KDACONV_EUNSUPPORTED;
-  if (dim * cs_stride1 * 4 > INT32_MAX) return KDACONV_EUNSUPPORTED;
-  if (batch == 0 || dim == 0) return KDACONV_OK;
-  if (!x || !weight || !conv_states || !cache_indices || !out) return KDACONV_EINVAL;
-  if (!aligned16(x) || !aligned16(out)) return KDACONV_EUNSUPPORTED;
 
   ConvParams P;
   fill_common(P, x, batch, x_row_stride, weight, weight_stride0, weight_stride1, bias,
@@ -1290,6 +1455,45 @@ extern "C" int kdaconv_packed_causal_conv1d_update(
       launch_update<kF16, kLaneChannels>(Q, cols, has_bias, silu, st);
     else
       launch_update<kBF16, kLaneChannels>(Q, cols, has_bias, silu, st);
+  });
+  return hipGetLastError() == hipSuccess ? KDACONV_OK : KDACONV_ELAUNCH;
+}
+
+extern "C" int kdaconv_packed_causal_conv1d_update_bf16_state(
+    const void* x, int dtype, int64_t batch, int64_t dim, int64_t x_row_stride,
+    const float* weight, int64_t weight_part_stride, int64_t weight_stride0,
+    int64_t weight_stride1, const float* bias, uint16_t* conv_states, int64_t num_cache_lines,
+    int64_t cs_stride0, int64_t cs_stride1, int64_t cs_stride2, const int32_t* cache_indices,
+    int64_t cache_indices_stride, int64_t part_dim, int activation, int has_null_block,
+    int64_t null_block_id, void* out, kdaconv_stream_t stream) {
+  const int rc = validate_update(x, dtype, batch, dim, x_row_stride, weight, weight_stride0,
+                                 weight_stride1, weight_part_stride, conv_states, 2,
+                                 num_cache_lines, cs_stride0, cs_stride1, cs_stride2,
+                                 cache_indices, cache_indices_stride, part_dim, activation, out);
+  if (rc != KDACONV_OK) return rc;
+  if (dtype != KDACONV_BF16) return KDACONV_EUNSUPPORTED;
+  if (batch == 0 || dim == 0) return KDACONV_OK;
+
+  ConvParams P;
+  fill_common(P, x, batch, x_row_stride, weight, weight_stride0, weight_stride1, bias,
+              reinterpret_cast<float*>(conv_states), num_cache_lines, cs_stride0, cs_stride1,
+              cs_stride2, cache_indices, cache_indices_stride, dim, part_dim, has_null_block,
+              null_block_id);
+  P.num_seqs = (int32_t)batch;
+  P.w_part_stride = weight_part_stride;
+  const int64_t parts = dim / part_dim;
+  const int64_t w_extent = (parts - 1) * weight_part_stride + part_dim + 3 * weight_stride1;
+  P.weight_vec = weight_stride0 == 4 && weight_stride1 == 1 && weight_part_stride == 4 * part_dim &&
+                 aligned16(weight);
+  P.weight_wm = weight_stride0 == 1 && weight_stride1 % 4 == 0 && weight_part_stride % 4 == 0 &&
+                aligned16(weight) && w_extent * 4 < INT32_MAX;
+  P.state_vec = cs_stride1 == 3 && cs_stride2 == 1 && cs_stride0 % 4 == 0 && aligned8(conv_states);
+  P.state_rows = 0;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const bool silu = activation == KDACONV_ACT_SILU;
+  const bool has_bias = bias != nullptr;
+  for_plane_groups(P, batch, dim, part_dim, 2, out, [&](ConvParams& Q, int64_t cols) {
+    launch_update<kBF16, kLaneChannels, kStateBF16>(Q, cols, has_bias, silu, st);
   });
   return hipGetLastError() == hipSuccess ? KDACONV_OK : KDACONV_ELAUNCH;
 }
@@ -1334,4 +1538,4 @@ extern "C" const char* kdaconv_status_string(int status) {
   }
 }
 
-extern "C" int kdaconv_version(void) { return 200; }
+extern "C" int kdaconv_version(void) { return 300; }

@@ -156,3 +156,55 @@ def test_update_status_codes(kw, code):
     """Argument checks of the decode entry point (they run before any HIP call)."""
     lib = _lib.load()
     assert lib.kdaconv_packed_causal_conv1d_update(*_update_args(**kw)) == code
+
+
+def _update_bf16_args(**kw):
+    a = dict(x=A, dt=_lib.BF16, B=64, dim=384, sx=384, w=A, wps=512, ws0=1, ws1=128, b=A, st=A,
+             lines=4, cs0=1152, cs1=3, cs2=1, ci=A, cis=1, pd=128, act=1, hn=0, nid=0, out=A)
+    a.update(kw)
+    return [a["x"], a["dt"], a["B"], a["dim"], a["sx"], a["w"], a["wps"], a["ws0"], a["ws1"],
+            a["b"], a["st"], a["lines"], a["cs0"], a["cs1"], a["cs2"], a["ci"], a["cis"],
+            a["pd"], a["act"], a["hn"], a["nid"], a["out"], None]
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=-1), _lib.EINVAL),
+    (dict(dt=7), _lib.EINVAL),
+    (dict(pd=100), _lib.EINVAL),
+    (dict(act=3), _lib.EINVAL),
+    (dict(x=0), _lib.EINVAL),
+    (dict(w=0), _lib.EINVAL),
+    (dict(st=0), _lib.EINVAL),
+    (dict(ci=0), _lib.EINVAL),
+    (dict(out=0), _lib.EINVAL),
+    (dict(dt=_lib.F16), _lib.EUNSUPPORTED),  # the page's gate: bf16 input only
+    (dict(dt=_lib.F32, sx=384), _lib.EUNSUPPORTED),
+    (dict(wps=-1), _lib.EUNSUPPORTED),
+    (dict(ws1=-128), _lib.EUNSUPPORTED),
+    (dict(cs1=-3), _lib.EUNSUPPORTED),
+    (dict(x=A + 2), _lib.EUNSUPPORTED),
+    (dict(dim=96, sx=96, pd=12), _lib.EUNSUPPORTED),
+    (dict(B=0, x=0, out=0), _lib.OK),  # nothing to do: no launch
+    (dict(dim=0), _lib.OK),
+])
+def test_update_bf16_state_status_codes(kw, code):
+    """Argument checks of the bf16-state decode entry point (before any HIP call)."""
+    lib = _lib.load()
+    assert lib.kdaconv_packed_causal_conv1d_update_bf16_state(*_update_bf16_args(**kw)) == code
+
+
+def test_python_bf16_state_checks():
+    """The binding's checks for a bf16 state run before the library is called."""
+    x = torch.zeros((4, 384), dtype=torch.float16)
+    st = torch.zeros((4, 384, 3), dtype=torch.bfloat16)
+    w = torch.zeros((3, 4, 128), dtype=torch.float32)
+    ci = torch.zeros(4, dtype=torch.int32)
+    xb = torch.zeros((4, 384), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        kd.packed_causal_conv1d_update(xb, w, None, st, ci, 128)
+    with pytest.raises(ValueError, match="bf16 x"):
+        kd.packed_causal_conv1d_update(x, w, None, st, ci, 128)
+    with pytest.raises(ValueError, match="width-major"):
+        kd.packed_causal_conv1d_update(xb, torch.zeros((3, 128, 4)), None, st, ci, 128)
+    assert kd._weight_strides(w, 128) == (512, 1, 128)
+    assert kd._weight_strides(torch.zeros((384, 4)), 128) == (512, 4, 1)

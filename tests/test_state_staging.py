@@ -111,3 +111,62 @@ def test_plane_groups_of_a_large_batch():
     many = _plane_groups(300000, 4608, 8, 4)
     assert len(many) == 1 or all(b % 8 == 0 for b, _ in many)
     _check_launch(300000, 4608, 8, 4)
+
+
+# ----------------------------------------------------------------- bf16 lines
+
+PIECES16 = 3 * V // 4  # 8-byte pieces per lane
+SLICE_READ16 = 8 * WAVE * PIECES16  # bytes of the slice the store instructions read
+
+
+def _check_wave_bf16(col_begin, col_end, cb):
+    """The bf16 staged write: lane l writes its 6 V bytes (3 V words) at bytes
+    [6 V slot, 6 V (slot + 1)) of the slice; piece q of lane l is bytes [8 (l + 64 q), +8),
+    stored at the same offset of the line part through a descriptor whose range is the
+    part's 6 n bytes."""
+    cfirst, n, lanes = _lanes(col_begin, col_end, cb)
+    part = 6 * n
+    assert part % 8 == 0 and SLICE_READ16 <= SLICE  # no straddling piece; reads in the slice
+    lds = {}
+    for lane, cl, slot in lanes:
+        for k in range(V):
+            for j in range(3):
+                b = 6 * V * slot + 2 * (3 * k + j)
+                assert 0 <= b and b + 2 <= SLICE
+                tag = (cl + k, j)
+                assert lds.get(b, tag) == tag
+                lds[b] = tag
+    stored = {}
+    for lane, _, _ in lanes:
+        for q in range(PIECES16):
+            off = 8 * (lane + WAVE * q)
+            assert 0 <= off and off + 8 <= SLICE_READ16
+            if off + 8 > part:  # at or past the range (part % 8 == 0): dropped
+                assert off >= part
+                continue
+            for w in range(4):
+                b = off + 2 * w
+                assert b not in stored
+                stored[b] = lds[b]
+    assert sorted(stored) == list(range(0, part, 2))
+    for b, (c, j) in stored.items():
+        assert c == cfirst + b // 6 and j == (b % 6) // 2
+        assert cfirst <= c < cfirst + n
+
+
+def _check_launch_bf16(tokens, dim, part_dim):
+    for col_begin, col_end in _plane_groups(tokens, dim, part_dim, 2):
+        cols = col_end - col_begin
+        for cb in range(-(-(cols // V) // WAVE)):
+            _check_wave_bf16(col_begin, col_end, cb)
+
+
+@pytest.mark.parametrize("batch", [64, 256, 1024, 4096])
+def test_bf16_state_bench_batches(batch):
+    _check_launch_bf16(batch, 4608, 1536)
+
+
+@pytest.mark.parametrize("dim,part_dim", [(3 * 256, 256), (3 * 200, 200), (3 * 40, 40),
+                                          (24, 8), (3 * 520, 520), (3 * 1536, 1536)])
+def test_bf16_state_test_shapes(dim, part_dim):
+    _check_launch_bf16(37, dim, part_dim)
