@@ -76,10 +76,12 @@ typedef enum kdaconv_dtype {
  *
  * x                  elements of format dtype; element (t, c) at
  *                    x[t * x_row_stride + c], rows t < num_tokens, channels c < dim.
- *                    Only columns [0, dim) are read. 16-byte aligned;
- *                    x_row_stride >= dim, and rows a multiple of 16 bytes apart
- *                    (x_row_stride a multiple of 8 for bf16 and fp16, of 4 for
- *                    FP32; else EUNSUPPORTED).
+ *                    Only columns [0, dim) are read. x_row_stride >= dim, any
+ *                    value (page: unit column stride, any row stride). x must be
+ *                    aligned to its element size (else EUNSUPPORTED). x and out
+ *                    16-byte aligned with rows a multiple of 16 bytes apart move as
+ *                    vectors; otherwise a slower path moves them element by element
+ *                    (a Q|K|V slice at any column offset).
  * dtype              KDACONV_BF16, KDACONV_F16 or KDACONV_F32 (else EINVAL): the
  *                    format of x and of out.
  * weight             FP32; tap k of channel c at weight[c * weight_stride0 +
@@ -109,8 +111,8 @@ typedef enum kdaconv_dtype {
  * null_block_id      when has_null_block != 0, sequences whose line equals
  *                    null_block_id skip the state (page: HAS_NULL_BLOCK).
  * out                elements of format dtype, dense (dim / part_dim, num_tokens,
- *                    part_dim), 16-byte aligned. Rows no sequence owns are left
- *                    unwritten.
+ *                    part_dim), aligned to the element size (see x). Rows no
+ *                    sequence owns are left unwritten.
  *
  * Device-data preconditions (not checked; violating them gives unspecified
  * values but no access outside the buffers described above): query_start_loc
@@ -144,7 +146,7 @@ int kdaconv_packed_causal_conv1d(
  * kdaconv_packed_causal_conv1d_update_bf16_state below.
  *
  * x                  elements of format dtype, (batch, dim) at row stride
- *                    x_row_stride (16-byte aligned rows, as for the prefill op).
+ *                    x_row_stride (alignment as for the prefill op).
  * weight, bias,
  * conv_states,
  * cache_indices,
@@ -154,7 +156,7 @@ int kdaconv_packed_causal_conv1d(
  * null_block_id      as for kdaconv_packed_causal_conv1d; cache_indices has one
  *                    entry per sequence of the batch.
  * out                elements of format dtype, dense (dim / part_dim, batch, part_dim),
- *                    16-byte aligned.
+ *                    aligned to the element size.
  *
  * Precondition (not checked): live lines distinct within the batch.
  * batch == 0 or dim == 0 returns KDACONV_OK with no launch. Status codes and
@@ -183,9 +185,9 @@ int kdaconv_packed_causal_conv1d_update(
  * and the token, whose words are kept unchanged (they are bf16 values already; a NaN
  * keeps its payload).
  *
- * x                  bf16 (batch, dim) at row stride x_row_stride (16-byte aligned
- *                    rows). dtype must be KDACONV_BF16 (the page's gate); fp16 and
- *                    FP32 give EUNSUPPORTED, unknown codes EINVAL.
+ * x                  bf16 (batch, dim) at row stride x_row_stride (alignment as for
+ *                    the prefill op). dtype must be KDACONV_BF16 (the page's gate);
+ *                    fp16 and FP32 give EUNSUPPORTED, unknown codes EINVAL.
  * weight             FP32; tap k of channel c at weight[(c / part_dim) *
  *                    weight_part_stride + (c % part_dim) * weight_stride0 + k *
  *                    weight_stride1]. The page's width-major (dim / part_dim, 4,

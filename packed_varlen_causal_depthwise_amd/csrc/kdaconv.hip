@@ -42,6 +42,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "kdaconv.h"
 #include "kdaconv_device.h"
@@ -118,6 +119,49 @@ struct Lane<16> {
   }
 };
 
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// The same per-lane vectors moved one element at a time, for x and out that are not
+// aligned to 16 bytes (a Q|K|V slice at any column offset, any row stride): 2-byte
+// loads and stores for bf16 and fp16, 4-byte ones for FP32. Pairs of 2-byte loads
+// fill the two halves of a word, which the compiler does without waiting for them.
+template <int kF, int V>
+struct LaneElems {
+  static constexpr int kB = element_bytes<kF>();
+  typedef typename Lane<V * kB>::vec vec;
+  template <int kPolicy>
+  static __device__ __forceinline__ vec load(__amdgpu_buffer_rsrc_t r, uint32_t vo, uint32_t so) {
+    vec v;
+    if (kB == 4) {
+#pragma unroll
+      for (int i = 0; i < V; ++i) v[i] = __builtin_amdgcn_raw_buffer_load_b32(r, vo + 4u * i, so, kPolicy);
+    } else {
+#pragma unroll
+      for (int i = 0; i < V / 2; ++i) {
+        u16x2 h;
+        h[0] = __builtin_amdgcn_raw_buffer_load_b16(r, vo + 4u * i, so, kPolicy);
+        h[1] = __builtin_amdgcn_raw_buffer_load_b16(r, vo + 4u * i + 2u, so, kPolicy);
+        v[i] = __builtin_bit_cast(uint32_t, h);
+      }
+    }
+    return v;
+  }
+  template <int kPolicy>
+  static __device__ __forceinline__ void store(vec v, __amdgpu_buffer_rsrc_t r, uint32_t vo,
+                                               uint32_t so) {
+    if (kB == 4) {
+#pragma unroll
+      for (int i = 0; i < V; ++i) __builtin_amdgcn_raw_buffer_store_b32(v[i], r, vo + 4u * i, so, kPolicy);
+    } else {
+#pragma unroll
+      for (int i = 0; i < V / 2; ++i) {
+        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(v[i] & 0xFFFFu), r, vo + 4u * i, so, kPolicy);
+        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(v[i] >> 16), r, vo + 4u * i + 2u, so, kPolicy);
+      }
+    }
+  }
+};
+
 struct ConvParams {
   const char* x;
   const float* weight;
@@ -163,6 +207,7 @@ struct ConvParams {
   int32_t bias_vec;  // bias is 16-byte aligned
   int32_t state_vec;  // each state line is (dim, 3) contiguous and 16-byte aligned
                       // (bf16 state: 8-byte aligned)
+  int32_t xo_vec;  // x and out 16-byte aligned, x rows a multiple of 16 bytes apart
   int32_t state_rows;  // each state line is 3 rows of dim contiguous channels ("dim first"),
                        // 16-byte aligned, row and line strides multiples of 4
 };
@@ -388,10 +433,12 @@ __device__ __forceinline__ Tile describe_tile(const ConvParams& P, int p, int la
 // The per-wave part of the convolution shared by the prefill and decode kernels:
 // the lane's channels, its weights and bias, the state line's I/O, prefill tiles
 // and decode steps.
-template <int kF, int V, int R, bool kBias, bool kSilu, int kS = kStateF32>
+template <int kF, int V, int R, bool kBias, bool kSilu, int kS = kStateF32, bool kA = true>
 struct ConvWorker {
   static constexpr int kBytes = element_bytes<kF>();
-  typedef Lane<V * kBytes> L;
+  // kA: x and out are 16-byte aligned with rows a multiple of 16 bytes apart, and move
+  // as one vector per lane and row; otherwise element by element.
+  typedef typename std::conditional<kA, Lane<V * kBytes>, LaneElems<kF, V>>::type L;
   typedef typename L::vec vec;
 
   const ConvParams& P;
@@ -1032,7 +1079,7 @@ struct ConvWorker {
 // kG adjacent column blocks (a column group). wave_slot maps the one-dimensional
 // launch to programs and column groups so that workgroups dispatched together cover
 // whole rows.
-template <int kF, int V, int R, int kG, bool kBias, bool kSilu>
+template <int kF, int V, int R, int kG, bool kBias, bool kSilu, bool kA>
 __global__ __launch_bounds__(kWave * kG) __attribute__((amdgpu_waves_per_eu(kMinWaves))) void packed_conv_kernel(const ConvParams P) {
   static_assert(V % 4 == 0, "the vector weight, bias and state paths take 4 channels at a time");
   const int lane = threadIdx.x % kWave;
@@ -1044,7 +1091,7 @@ __global__ __launch_bounds__(kWave * kG) __attribute__((amdgpu_waves_per_eu(kMin
   // Weights first: their loads overlap the search for the tile's sequence.
   __shared__ uint2 fix_slots[kG][kFixCapacity];
   __shared__ float stage[kG][3 * V * kWave];
-  ConvWorker<kF, V, R, kBias, kSilu> w(P, lane, cb, fix_slots[wave], stage[wave]);
+  ConvWorker<kF, V, R, kBias, kSilu, kStateF32, kA> w(P, lane, cb, fix_slots[wave], stage[wave]);
   w.load_weights();
   const Tile d = describe_tile<R>(P, p, lane);
   if (!d.valid) return;
@@ -1076,7 +1123,7 @@ __global__ __launch_bounds__(kWave * kG) __attribute__((amdgpu_waves_per_eu(kMin
 // Decode update: program p is sequences kSeq p .. kSeq p + kSeq - 1 (rows of x), one
 // wave per column block, kG column blocks per workgroup. No search: every sequence
 // has exactly one token.
-template <int kF, int V, int kSeq, int kG, bool kBias, bool kSilu, int kS>
+template <int kF, int V, int kSeq, int kG, bool kBias, bool kSilu, int kS, bool kA>
 __global__ __launch_bounds__(kWave * kG) void packed_conv_update_kernel(const ConvParams P) {
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
@@ -1085,7 +1132,7 @@ __global__ __launch_bounds__(kWave * kG) void packed_conv_update_kernel(const Co
   const int cb = slot.cb;
   if (cb >= P.col_blocks) return;
   __shared__ float stage[kG][3 * V * kWave];
-  ConvWorker<kF, V, 1, kBias, kSilu, kS> w(P, lane, cb, nullptr, stage[wave]);
+  ConvWorker<kF, V, 1, kBias, kSilu, kS, kA> w(P, lane, cb, nullptr, stage[wave]);
   w.load_weights();
   if (P.state_vec)
     w.template decode_many<kSeq, true>(p * kSeq);
@@ -1141,6 +1188,13 @@ __global__ __launch_bounds__(kWave) void activation_map_kernel(uint32_t first, u
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned8(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
+bool element_aligned(const void* p, int64_t eb) {
+  return (reinterpret_cast<uintptr_t>(p) & (uintptr_t)(eb - 1)) == 0;
+}
+// x and out take the vector path: 16-byte aligned, x rows a multiple of 16 bytes apart.
+bool vector_io(const void* x, int64_t x_row_stride, int64_t eb, const void* out) {
+  return aligned16(x) && aligned16(out) && (x_row_stride * eb) % 16 == 0;
+}
 
 bool known_dtype(int dtype) { return dtype == kBF16 || dtype == kF16 || dtype == kF32; }
 
@@ -1157,8 +1211,8 @@ int validate(const void* x, int dtype, int64_t num_tokens, int64_t dim, int64_t 
   if (x_row_stride < dim) return KDACONV_EINVAL;
   if (activation != KDACONV_ACT_NONE && activation != KDACONV_ACT_SILU) return KDACONV_EINVAL;
   const int64_t eb = dtype_bytes(dtype);
-  // Rows and plane columns start on 16-byte boundaries.
-  if (part_dim % 8 != 0 || (x_row_stride * eb) % 16 != 0) return KDACONV_EUNSUPPORTED;
+  // Plane rows are whole 16-byte pieces (x and its rows may be unaligned: element path).
+  if (part_dim % 8 != 0) return KDACONV_EUNSUPPORTED;
   if (ws0 < 0 || ws1 < 0 || cs0 < 0 || cs1 < 0 || cs2 < 0 || ci_stride < 0)
     return KDACONV_EUNSUPPORTED;
   // int32 token and sequence indices; 32-bit offsets within a program's rows
@@ -1173,7 +1227,7 @@ int validate(const void* x, int dtype, int64_t num_tokens, int64_t dim, int64_t 
   if (dim * cs1 * 4 > INT32_MAX) return KDACONV_EUNSUPPORTED;
   if (num_tokens == 0 || num_seqs == 0 || dim == 0) return KDACONV_OK;
   if (!x || !weight || !conv_states || !qsl || !ci || !out) return KDACONV_EINVAL;
-  if (!aligned16(x) || !aligned16(out)) return KDACONV_EUNSUPPORTED;
+  if (!element_aligned(x, eb) || !element_aligned(out, eb)) return KDACONV_EUNSUPPORTED;
   return KDACONV_OK;
 }
 
@@ -1190,7 +1244,7 @@ int validate_update(const void* x, int dtype, int64_t batch, int64_t dim, int64_
   if (x_row_stride < dim) return KDACONV_EINVAL;
   if (activation != KDACONV_ACT_NONE && activation != KDACONV_ACT_SILU) return KDACONV_EINVAL;
   const int64_t eb = dtype_bytes(dtype);
-  if (part_dim % 8 != 0 || (x_row_stride * eb) % 16 != 0) return KDACONV_EUNSUPPORTED;
+  if (part_dim % 8 != 0) return KDACONV_EUNSUPPORTED;
   if (ws0 < 0 || ws1 < 0 || wps < 0 || cs0 < 0 || cs1 < 0 || cs2 < 0 || ci_stride < 0)
     return KDACONV_EUNSUPPORTED;
   if (batch > INT32_MAX - 1 || dim > INT32_MAX / 2) return KDACONV_EUNSUPPORTED;
@@ -1200,11 +1254,11 @@ int validate_update(const void* x, int dtype, int64_t batch, int64_t dim, int64_
   if (dim * cs1 * state_bytes > INT32_MAX) return KDACONV_EUNSUPPORTED;
   if (batch == 0 || dim == 0) return KDACONV_OK;
   if (!x || !weight || !conv_states || !cache_indices || !out) return KDACONV_EINVAL;
-  if (!aligned16(x) || !aligned16(out)) return KDACONV_EUNSUPPORTED;
+  if (!element_aligned(x, eb) || !element_aligned(out, eb)) return KDACONV_EUNSUPPORTED;
   return KDACONV_OK;
 }
 
-template <int kF, int V, int kG>
+template <int kF, int V, int kG, bool kA>
 void launch_group(ConvParams P, bool bias, bool silu, hipStream_t st) {
   constexpr int R = rows_per_tile<kF>();
   const uint64_t groups = ((uint64_t)P.col_blocks + kG - 1) / kG;
@@ -1213,14 +1267,14 @@ void launch_group(ConvParams P, bool bias, bool silu, hipStream_t st) {
   const dim3 block(kWave * kG);
   if (bias) {
     if (silu)
-      hipLaunchKernelGGL((packed_conv_kernel<kF, V, R, kG, true, true>), grid, block, 0, st, P);
+      hipLaunchKernelGGL((packed_conv_kernel<kF, V, R, kG, true, true, kA>), grid, block, 0, st, P);
     else
-      hipLaunchKernelGGL((packed_conv_kernel<kF, V, R, kG, true, false>), grid, block, 0, st, P);
+      hipLaunchKernelGGL((packed_conv_kernel<kF, V, R, kG, true, false, kA>), grid, block, 0, st, P);
   } else {
     if (silu)
-      hipLaunchKernelGGL((packed_conv_kernel<kF, V, R, kG, false, true>), grid, block, 0, st, P);
+      hipLaunchKernelGGL((packed_conv_kernel<kF, V, R, kG, false, true, kA>), grid, block, 0, st, P);
     else
-      hipLaunchKernelGGL((packed_conv_kernel<kF, V, R, kG, false, false>), grid, block, 0, st, P);
+      hipLaunchKernelGGL((packed_conv_kernel<kF, V, R, kG, false, false, kA>), grid, block, 0, st, P);
   }
 }
 
@@ -1241,13 +1295,16 @@ void launch(ConvParams P, int64_t cols, bool bias, bool silu, hipStream_t st) {
   // Two waves per workgroup measured 3-4 % faster on the 16384 x 4608 bf16
   // workload; with an odd number of column blocks the second wave of every last
   // workgroup would idle, and one wave per workgroup is kept.
-  if (P.col_blocks % 2 == 0)
-    launch_group<kF, V, 2>(P, bias, silu, st);
+  // Unaligned x or out (element loads and stores) take one wave per workgroup only.
+  if (!P.xo_vec)
+    launch_group<kF, V, 1, false>(P, bias, silu, st);
+  else if (P.col_blocks % 2 == 0)
+    launch_group<kF, V, 2, true>(P, bias, silu, st);
   else
-    launch_group<kF, V, 1>(P, bias, silu, st);
+    launch_group<kF, V, 1, true>(P, bias, silu, st);
 }
 
-template <int kF, int V, int kSeq, int kG, int kS>
+template <int kF, int V, int kSeq, int kG, int kS, bool kA>
 void launch_update_group(ConvParams P, bool bias, bool silu, hipStream_t st) {
   const uint64_t groups = ((uint64_t)P.col_blocks + kG - 1) / kG;
   set_wave_order(P, groups, false);
@@ -1255,24 +1312,27 @@ void launch_update_group(ConvParams P, bool bias, bool silu, hipStream_t st) {
   const dim3 block(kWave * kG);
   if (bias) {
     if (silu)
-      hipLaunchKernelGGL((packed_conv_update_kernel<kF, V, kSeq, kG, true, true, kS>), grid, block, 0, st, P);
+      hipLaunchKernelGGL((packed_conv_update_kernel<kF, V, kSeq, kG, true, true, kS, kA>), grid, block, 0, st, P);
     else
-      hipLaunchKernelGGL((packed_conv_update_kernel<kF, V, kSeq, kG, true, false, kS>), grid, block, 0, st, P);
+      hipLaunchKernelGGL((packed_conv_update_kernel<kF, V, kSeq, kG, true, false, kS, kA>), grid, block, 0, st, P);
   } else {
     if (silu)
-      hipLaunchKernelGGL((packed_conv_update_kernel<kF, V, kSeq, kG, false, true, kS>), grid, block, 0, st, P);
+      hipLaunchKernelGGL((packed_conv_update_kernel<kF, V, kSeq, kG, false, true, kS, kA>), grid, block, 0, st, P);
     else
-      hipLaunchKernelGGL((packed_conv_update_kernel<kF, V, kSeq, kG, false, false, kS>), grid, block, 0, st, P);
+      hipLaunchKernelGGL((packed_conv_update_kernel<kF, V, kSeq, kG, false, false, kS, kA>), grid, block, 0, st, P);
   }
 }
 
-template <int kF, int V, int kSeq, int kS>
+template <int kF, int V, int kSeq, int kS, bool kA>
 void launch_update_seq(ConvParams P, bool bias, bool silu, hipStream_t st) {
   P.programs = (P.num_seqs + kSeq - 1) / kSeq;
-  if (P.col_blocks % 2 == 0)
-    launch_update_group<kF, V, kSeq, 2, kS>(P, bias, silu, st);
-  else
-    launch_update_group<kF, V, kSeq, 1, kS>(P, bias, silu, st);
+  if constexpr (kA) {
+    if (P.col_blocks % 2 == 0) {
+      launch_update_group<kF, V, kSeq, 2, kS, true>(P, bias, silu, st);
+      return;
+    }
+  }
+  launch_update_group<kF, V, kSeq, 1, kS, kA>(P, bias, silu, st);
 }
 
 // Sequences per decode wave: as many as keep at least 2048 waves in the launch (two per
@@ -1284,12 +1344,16 @@ template <int kF, int V, int kS = kStateF32>
 void launch_update(ConvParams P, int64_t cols, bool bias, bool silu, hipStream_t st) {
   P.col_blocks = (int32_t)((cols / V + kWave - 1) / kWave);
   const int64_t waves1 = (int64_t)P.num_seqs * P.col_blocks;
-  if (waves1 >= 4 * 2048)
-    launch_update_seq<kF, V, 4, kS>(P, bias, silu, st);
+  // Unaligned x or out (element loads and stores): one sequence per wave, one wave per
+  // workgroup.
+  if (!P.xo_vec)
+    launch_update_seq<kF, V, 1, kS, false>(P, bias, silu, st);
+  else if (waves1 >= 4 * 2048)
+    launch_update_seq<kF, V, 4, kS, true>(P, bias, silu, st);
   else if (waves1 >= 2 * 2048)
-    launch_update_seq<kF, V, 2, kS>(P, bias, silu, st);
+    launch_update_seq<kF, V, 2, kS, true>(P, bias, silu, st);
   else
-    launch_update_seq<kF, V, 1, kS>(P, bias, silu, st);
+    launch_update_seq<kF, V, 1, kS, true>(P, bias, silu, st);
 }
 
 // Fields of ConvParams shared by both operations.
@@ -1403,6 +1467,7 @@ extern "C" int kdaconv_packed_causal_conv1d(
   P.qsl = query_start_loc;
   P.has_init = has_initial_state;
   P.num_seqs = (int32_t)num_seqs;
+  P.xo_vec = vector_io(x, x_row_stride, eb, out);
   int levels = 0;
   int64_t reach = 1;
   while (reach < num_seqs) {
@@ -1445,6 +1510,7 @@ extern "C" int kdaconv_packed_causal_conv1d_update(
               conv_states, num_cache_lines, cs_stride0, cs_stride1, cs_stride2, cache_indices,
               cache_indices_stride, dim, part_dim, has_null_block, null_block_id);
   P.num_seqs = (int32_t)batch;
+  P.xo_vec = vector_io(x, x_row_stride, eb, out);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const bool silu = activation == KDACONV_ACT_SILU;
   const bool has_bias = bias != nullptr;
@@ -1480,6 +1546,7 @@ extern "C" int kdaconv_packed_causal_conv1d_update_bf16_state(
               cs_stride2, cache_indices, cache_indices_stride, dim, part_dim, has_null_block,
               null_block_id);
   P.num_seqs = (int32_t)batch;
+  P.xo_vec = vector_io(x, x_row_stride, 2, out);
   P.w_part_stride = weight_part_stride;
   const int64_t parts = dim / part_dim;
   const int64_t w_extent = (parts - 1) * weight_part_stride + part_dim + 3 * weight_stride1;

@@ -68,9 +68,13 @@ def _args(**kw):
     (dict(b=0), _lib.OK),  # no bias
     (dict(init=0), _lib.OK),  # no initial states
     (dict(dim=96, sx=96, pd=12), _lib.EUNSUPPORTED),  # part_dim not a multiple of 8
-    (dict(sx=390), _lib.EUNSUPPORTED),  # row stride not a multiple of 8
-    (dict(x=A + 2), _lib.EUNSUPPORTED),  # x not 16-byte aligned
-    (dict(out=A + 8), _lib.EUNSUPPORTED),
+    (dict(sx=390), _lib.OK),  # rows not 16 bytes apart: element path
+    (dict(x=A + 2), _lib.OK),  # x at an odd column: element path
+    (dict(out=A + 8), _lib.OK),
+    (dict(x=A + 1), _lib.EUNSUPPORTED),  # not aligned to the element size
+    (dict(out=A + 1), _lib.EUNSUPPORTED),
+    (dict(dt=_lib.F32, x=A + 2), _lib.EUNSUPPORTED),
+    (dict(dt=_lib.F32, x=A + 4, sx=385), _lib.OK),
     (dict(cs1=-3), _lib.EUNSUPPORTED),
     (dict(T=0, x=0, out=0), _lib.OK),  # nothing to do: no launch, pointers unused
     (dict(S=0, qsl=0), _lib.OK),
@@ -79,9 +83,9 @@ def _args(**kw):
     (dict(dt=-1), _lib.EINVAL),
     (dict(dt=_lib.F16), _lib.OK),
     (dict(dt=_lib.F32), _lib.OK),
-    (dict(dt=_lib.F16, sx=388), _lib.EUNSUPPORTED),  # fp16 rows 776 bytes apart
+    (dict(dt=_lib.F16, sx=388), _lib.OK),  # fp16 rows 776 bytes apart: element path
     (dict(dt=_lib.F32, sx=388), _lib.OK),  # FP32 rows 1552 bytes apart
-    (dict(dt=_lib.F32, sx=386), _lib.EUNSUPPORTED),
+    (dict(dt=_lib.F32, sx=386), _lib.OK),
     (dict(dt=_lib.F32, T=1 << 25, pd=8, dim=8, sx=8), _lib.EUNSUPPORTED),  # plane of 2^30 bytes
     (dict(dt=_lib.BF16, T=1 << 25, pd=8, dim=8, sx=8), _lib.OK),
 ])
@@ -146,9 +150,9 @@ def _update_args(**kw):
     (dict(ci=0), _lib.EINVAL),
     (dict(out=0), _lib.EINVAL),
     (dict(dim=96, sx=96, pd=12), _lib.EUNSUPPORTED),
-    (dict(sx=390), _lib.EUNSUPPORTED),
-    (dict(x=A + 2), _lib.EUNSUPPORTED),
-    (dict(out=A + 8), _lib.EUNSUPPORTED),
+    (dict(x=A + 1), _lib.EUNSUPPORTED),
+    (dict(out=A + 1), _lib.EUNSUPPORTED),
+    (dict(dt=_lib.F32, x=A + 2), _lib.EUNSUPPORTED),
     (dict(cs2=-1), _lib.EUNSUPPORTED),
     (dict(B=0, x=0, out=0), _lib.OK),  # nothing to do: no launch
 ])
@@ -182,7 +186,8 @@ def _update_bf16_args(**kw):
     (dict(wps=-1), _lib.EUNSUPPORTED),
     (dict(ws1=-128), _lib.EUNSUPPORTED),
     (dict(cs1=-3), _lib.EUNSUPPORTED),
-    (dict(x=A + 2), _lib.EUNSUPPORTED),
+    (dict(x=A + 1), _lib.EUNSUPPORTED),
+    (dict(out=A + 3), _lib.EUNSUPPORTED),
     (dict(dim=96, sx=96, pd=12), _lib.EUNSUPPORTED),
     (dict(B=0, x=0, out=0), _lib.OK),  # nothing to do: no launch
     (dict(dim=0), _lib.OK),
