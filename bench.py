@@ -175,11 +175,12 @@ def fmt_label(x_dtype: str) -> str:
 
 
 def time_config(kd, torch, wl, steps: int, warmup: int, blocks: int = 10, decode: bool = False,
-                settle_ms: float = 30.0):
+                settle_ms: float = 30.0, x_column: int = 0):
     """Back-to-back per-launch times of the conv (or, with decode, of the decode step) on
     one workload, with complete input/output/state sets rotated past the Infinity Cache.
     A ``workloads.Bf16StateDecode`` is timed as the decode step with its bf16 state and
-    width-major weight."""
+    width-major weight. With x_column > 0, x is read from a buffer whose columns start that
+    many elements in (x not 16-byte aligned: the element-by-element path)."""
     dev = torch.device("cuda:0")
     bf16_state = not hasattr(wl, "query_start_loc")
     tokens = wl.batch if bf16_state else wl.num_tokens
@@ -187,6 +188,12 @@ def time_config(kd, torch, wl, steps: int, warmup: int, blocks: int = 10, decode
     P = wl.dim // wl.part_dim
     if bf16_state:
         xb = torch.from_numpy(wl.x.view(np.int16)).to(dev).view(torch.bfloat16)
+    elif x_column:
+        raw = np.zeros((wl.x.shape[0], wl.x.shape[1] + x_column), dtype=wl.x.dtype)
+        raw[:, x_column:] = wl.x
+        signed = np.int32 if raw.dtype == np.uint32 else np.int16
+        dt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[wl.x_dtype]
+        xb = torch.from_numpy(raw.view(signed)).to(dev).view(dt)[:, x_column:]
     else:
         xb = x_tensor(torch, wl, dev)
     eb = xb.element_size()
@@ -194,7 +201,12 @@ def time_config(kd, torch, wl, steps: int, warmup: int, blocks: int = 10, decode
     sets = rotation_sets(set_bytes)
     bufs = []
     for i in range(sets):
-        x = xb.clone() if i else xb
+        if x_column:  # a copy of the whole buffer, so that every set keeps the offset
+            x = xb if not i else xb.as_strided(
+                (xb.shape[0], xb.shape[1] + x_column), (xb.stride(0), 1),
+                xb.storage_offset() - x_column).clone()[:, x_column:]
+        else:
+            x = xb.clone() if i else xb
         st = torch.from_numpy(wl.conv_states.copy().view(np.int16) if bf16_state
                               else wl.conv_states.copy()).to(dev)
         bufs.append(dict(
@@ -223,7 +235,9 @@ def time_config(kd, torch, wl, steps: int, warmup: int, blocks: int = 10, decode
     for i in range(warmup):
         step(n + i)
     us = back_to_back(torch, stream, step, steps, blocks)
-    res = {"workload": wl.name + f", x and out {fmt_label(x_dtype)}", "buffer_sets_rotated": sets}
+    res = {"workload": wl.name + f", x and out {fmt_label(x_dtype)}"
+                       + (f", x from column {x_column} of its buffer" if x_column else ""),
+           "buffer_sets_rotated": sets}
     res.update(summary(wl.algorithmic_bytes(), us))
     del bufs
     torch.cuda.empty_cache()
@@ -247,79 +261,71 @@ def device_info(torch, dev) -> dict:
             "memory_gib": round(props.total_memory / 2**30, 1)}
 
 
-class ClockSampler:
-    """Polls the GPU's core (GFX) and memory clocks in a background thread through amdsmi
-    (the interface torch.cuda.clock_rate uses on ROCm), every 5 ms while sampling is
-    on: over the settle phase and the spread blocks of the headline workload, which
-    bracket the timed region. It is paused during the timed region itself, where the
-    thread's turns at the interpreter lock could delay the launches. Best effort: if
-    amdsmi is missing or refuses, the error is reported instead."""
+def clocks_under_load(torch, dev, step, seconds: float = 3.0, first: int = 0) -> dict:
+    """The GPU's clocks while the headline workload runs back to back for `seconds`.
 
-    def __init__(self, torch, dev, period_s: float = 0.005):
-        import threading
+    The readings come from amdsmi's GPU metrics (the interface torch.cuda.clock_rate uses
+    on ROCm), which the power management refreshes about once a second, so a short
+    window would only see the readings from before it. A background thread polls every
+    20 ms; only readings refreshed at least 1.1 s into the busy window are kept, one per
+    refresh. Reported: the core clock of the socket and of each XCD, the memory clock,
+    the socket power and the activity. Best effort: if amdsmi is missing or refuses, the
+    error is reported instead."""
+    import threading
 
-        self.period = period_s
-        self.samples = {"gfx": [], "mem": []}
-        self.error = None
-        self._on = threading.Event()
-        self._stop = threading.Event()
-        self._thread = None
-        try:
-            import amdsmi
+    try:
+        import amdsmi
 
-            self._amdsmi = amdsmi
-            self._handle = torch.cuda._get_amdsmi_handler(dev)
-            self._read(keep=False)
-        except Exception as e:  # noqa: BLE001 - reported, not raised
-            self.error = f"{type(e).__name__}: {e}"
-            return
-        self._thread = threading.Thread(target=self._run, daemon=True)
-        self._thread.start()
+        handle = torch.cuda._get_amdsmi_handler(dev)
+        amdsmi.amdsmi_get_gpu_metrics_info(handle)
+    except Exception as e:  # noqa: BLE001 - reported, not raised
+        return {"error": f"{type(e).__name__}: {e}"}
+    seen = {}
+    stop = threading.Event()
+    errors = []
+    t0 = time.perf_counter()
 
-    def _read(self, keep: bool = True):
-        a = self._amdsmi
-        for key, kind in (("gfx", a.AmdSmiClkType.GFX), ("mem", a.AmdSmiClkType.MEM)):
-            v = a.amdsmi_get_clock_info(self._handle, kind).get("clk")
-            if keep and isinstance(v, (int, float)):
-                self.samples[key].append(float(v))
-
-    def _run(self):
-        while not self._stop.is_set():
-            self._on.wait(0.05)
-            if self._stop.wait(self.period) or not self._on.is_set():
-                continue
+    def poll():
+        while not stop.wait(0.02):
             try:
-                self._read()
+                m = amdsmi.amdsmi_get_gpu_metrics_info(handle)
             except Exception as e:  # noqa: BLE001
-                self.error = f"{type(e).__name__}: {e}"
+                errors.append(f"{type(e).__name__}: {e}")
                 return
+            ts = m.get("firmware_timestamp")
+            if ts not in seen:
+                seen[ts] = (time.perf_counter() - t0, m)
 
-    def resume(self):
-        self._on.set()
+    th = threading.Thread(target=poll, daemon=True)
+    th.start()
+    torch.cuda.synchronize()
+    t_busy = time.perf_counter() - t0
+    done = 0
+    while time.perf_counter() - t0 < t_busy + seconds:
+        for _ in range(50):
+            step(first + done)
+            done += 1
+        torch.cuda.synchronize()
+    t_end = time.perf_counter() - t0
+    stop.set()
+    th.join()
+    keep = [m for t, m in seen.values() if t_busy + 1.1 <= t <= t_end]
 
-    def pause(self):
-        self._on.clear()
+    def num(v):
+        return v if isinstance(v, (int, float)) else None
 
-    def stop(self):
-        self._on.clear()
-        self._stop.set()
-        if self._thread is not None:
-            self._thread.join()
-
-    def report(self) -> dict:
-        if self.error and not self.samples["gfx"]:
-            return {"error": self.error}
-        out = {"source": "amdsmi_get_clock_info, polled every 5 ms",
-               "window": "the settle phase and the spread blocks of the headline workload "
-                         "(paused during the timed region between them)"}
-        for key in ("gfx", "mem"):
-            v = np.array(self.samples[key])
-            if v.size:
-                out[f"{key}_mhz"] = {"median": float(np.median(v)), "min": float(v.min()),
-                                     "max": float(v.max()), "samples": int(v.size)}
-        if self.error:
-            out["error"] = self.error
-        return out
+    out = {"source": "amdsmi GPU metrics (refreshed about once a second), during "
+                     f"{seconds:.0f} s of back-to-back headline steps after the timed blocks",
+           "launches": done, "readings": len(keep)}
+    if keep:
+        out["gfx_mhz"] = [num(m.get("current_gfxclk")) for m in keep]
+        out["gfx_mhz_per_xcd"] = [list(m.get("current_gfxclks") or [])[:8] for m in keep]
+        out["memory_clock_mhz"] = [num(m.get("current_uclk")) for m in keep]
+        out["socket_power_w"] = [num(m.get("current_socket_power")) for m in keep]
+        out["gfx_activity_pct"] = [num(m.get("average_gfx_activity")) for m in keep]
+    if errors:
+        out["error"] = errors[0]
+    return out
 
 
 def oracle_on_channel_slices(oracle, wl, threads: int):
@@ -409,6 +415,9 @@ def main() -> int:
     ap.add_argument("--spread-blocks", type=int, default=5,
                     help="after the timed region, this many more blocks of K back-to-back steps "
                          "give the median and p10/p90 of the per-launch time")
+    ap.add_argument("--clock-seconds", type=float, default=3.0,
+                    help="seconds of back-to-back steps after the timed blocks during which the "
+                         "GPU's clocks are read (0 skips)")
     ap.add_argument("--cpu-runs", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-configs", action="store_true",
@@ -468,10 +477,7 @@ def main() -> int:
     for i in range(args.warmup):
         step(i)
     first_us = back_to_back(torch, stream, step, args.steps, 1)[0]
-    clocks = ClockSampler(torch, dev)
-    clocks.resume()
     settled = settle(torch, step, args.settle_ms)
-    clocks.pause()
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize(dev)
@@ -491,9 +497,9 @@ def main() -> int:
 
     # Spread: more blocks of K back-to-back steps timed the same way, one per-launch mean
     # per block.
-    clocks.resume()
     blocks_us = back_to_back(torch, stream, step, args.steps, args.spread_blocks)
-    clocks.stop()
+    clocks = clocks_under_load(torch, dev, step, args.clock_seconds) if args.clock_seconds > 0 \
+        else {"skipped": True}
 
     value = nbytes / (ms_per_step * 1e-3) / 1e9
     result = {
@@ -513,7 +519,7 @@ def main() -> int:
         "dtype": "bf16",
         "data": "synthetic",
         "device": device_info(torch, dev),
-        "clocks": clocks.report(),
+        "clocks": clocks,
         "config": {
             "workload": "packed varlen causal depthwise conv: 1 sequence x 16384 tokens, "
                         "dim 4608 = 3 x 1536, bf16 x read in place from rows of 9728, bf16 "
@@ -561,6 +567,9 @@ def main() -> int:
             fmt: time_config(kd, torch, workloads.config3(x_dtype=fmt), steps=20, warmup=5)
             for fmt in ("f16", "f32")
         }
+        # The headline workload with x read from column 1 of its buffer (not 16-byte
+        # aligned): the element-by-element path.
+        result["unaligned_x"] = time_config(kd, torch, wl, steps=20, warmup=5, x_column=1)
         # Context: one sequence of 2K-8K tokens (the first rows of the headline workload).
         result["context_sweep"] = {}
         for tokens in (2048, 4096, 8192):
