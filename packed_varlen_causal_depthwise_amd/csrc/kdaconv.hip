@@ -122,7 +122,7 @@ struct Lane<16> {
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 // The same per-lane vectors moved one element at a time, for x and out that are not
-// aligned to 16 bytes (a Q|K|V slice at any column offset, any row stride): 2-byte
+// aligned to the vector (a Q|K|V slice at any column offset, any row stride): 2-byte
 // loads and stores for bf16 and fp16, 4-byte ones for FP32. Pairs of 2-byte loads
 // fill the two halves of a word, which the compiler does without waiting for them.
 template <int kF, int V>
@@ -207,7 +207,7 @@ struct ConvParams {
   int32_t bias_vec;  // bias is 16-byte aligned
   int32_t state_vec;  // each state line is (dim, 3) contiguous and 16-byte aligned
                       // (bf16 state: 8-byte aligned)
-  int32_t xo_vec;  // x and out 16-byte aligned, x rows a multiple of 16 bytes apart
+  int32_t xo_vec;  // x, out and the x row pitch aligned to the lane's vector
   int32_t state_rows;  // each state line is 3 rows of dim contiguous channels ("dim first"),
                        // 16-byte aligned, row and line strides multiples of 4
 };
@@ -436,8 +436,8 @@ __device__ __forceinline__ Tile describe_tile(const ConvParams& P, int p, int la
 template <int kF, int V, int R, bool kBias, bool kSilu, int kS = kStateF32, bool kA = true>
 struct ConvWorker {
   static constexpr int kBytes = element_bytes<kF>();
-  // kA: x and out are 16-byte aligned with rows a multiple of 16 bytes apart, and move
-  // as one vector per lane and row; otherwise element by element.
+  // kA: x, out and the x row pitch are aligned to the lane's vector of V elements, which
+  // moves as one load or store per row; otherwise element by element.
   typedef typename std::conditional<kA, Lane<V * kBytes>, LaneElems<kF, V>>::type L;
   typedef typename L::vec vec;
 
@@ -1191,9 +1191,13 @@ bool aligned8(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0
 bool element_aligned(const void* p, int64_t eb) {
   return (reinterpret_cast<uintptr_t>(p) & (uintptr_t)(eb - 1)) == 0;
 }
-// x and out take the vector path: 16-byte aligned, x rows a multiple of 16 bytes apart.
+// x and out take the vector path when every lane's vector (4 elements: 8 bytes for bf16
+// and fp16, 16 for FP32) is naturally aligned: x, out and the x row pitch are multiples
+// of the vector size.
 bool vector_io(const void* x, int64_t x_row_stride, int64_t eb, const void* out) {
-  return aligned16(x) && aligned16(out) && (x_row_stride * eb) % 16 == 0;
+  const uintptr_t vb = (uintptr_t)(kLaneChannels * eb);
+  return (reinterpret_cast<uintptr_t>(x) % vb) == 0 && (reinterpret_cast<uintptr_t>(out) % vb) == 0 &&
+         (x_row_stride * eb) % (int64_t)vb == 0;
 }
 
 bool known_dtype(int dtype) { return dtype == kBF16 || dtype == kF16 || dtype == kF32; }
