@@ -116,6 +116,36 @@ def queue_ahead(torch):
     torch.cuda._sleep(400_000)
 
 
+def graph_replays(torch, step, steps: int, blocks: int):
+    """Per-launch times of `blocks` replays of one HIP graph holding `steps` launches (the
+    steps captured once on a side stream), timed back to back between events on the
+    replay stream. Serving loops launch short kernels this way; the host's time per call
+    then falls outside the GPU's critical path."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(0)  # first use on the capture stream, outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(steps):
+            step(i)
+    torch.cuda.synchronize()
+    g.replay()  # warm
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(blocks + 1)]
+    queue_ahead(torch)
+    evs[0].record(stream)
+    for b in range(blocks):
+        g.replay()
+        evs[b + 1].record(stream)
+    torch.cuda.synchronize()
+    del g
+    return np.array([evs[b].elapsed_time(evs[b + 1]) * 1e3 / steps for b in range(blocks)])
+
+
 def back_to_back(torch, stream, step, steps: int, blocks: int):
     """Per-launch times of `blocks` blocks of `steps` back-to-back launches, with an event
     only at each block boundary (events between single launches put an idle gap in front of
@@ -175,12 +205,15 @@ def fmt_label(x_dtype: str) -> str:
 
 
 def time_config(kd, torch, wl, steps: int, warmup: int, blocks: int = 10, decode: bool = False,
-                settle_ms: float = 30.0, x_column: int = 0):
+                settle_ms: float = 30.0, x_column: int = 0, graph: bool = False):
     """Back-to-back per-launch times of the conv (or, with decode, of the decode step) on
     one workload, with complete input/output/state sets rotated past the Infinity Cache.
     A ``workloads.Bf16StateDecode`` is timed as the decode step with its bf16 state and
     width-major weight. With x_column > 0, x is read from a buffer whose columns start that
-    many elements in (x not 16-byte aligned: the element-by-element path)."""
+    many elements in (x not 16-byte aligned: the element-by-element path). With graph, the
+    same steps are also captured in a HIP graph and replayed (``graph``): for launches
+    shorter than the binding's host time per call, the eager figure is the host's rate
+    and the replayed one the GPU's."""
     dev = torch.device("cuda:0")
     bf16_state = not hasattr(wl, "query_start_loc")
     tokens = wl.batch if bf16_state else wl.num_tokens
@@ -235,10 +268,13 @@ def time_config(kd, torch, wl, steps: int, warmup: int, blocks: int = 10, decode
     for i in range(warmup):
         step(n + i)
     us = back_to_back(torch, stream, step, steps, blocks)
+    graph_us = graph_replays(torch, step, steps, blocks) if graph else None
     res = {"workload": wl.name + f", x and out {fmt_label(x_dtype)}"
                        + (f", x from column {x_column} of its buffer" if x_column else ""),
            "buffer_sets_rotated": sets}
     res.update(summary(wl.algorithmic_bytes(), us))
+    if graph_us is not None:
+        res["graph"] = summary(wl.algorithmic_bytes(), graph_us)
     del bufs
     torch.cuda.empty_cache()
     return res
@@ -547,20 +583,21 @@ def main() -> int:
         # The other workloads are parity cases; their rates are reported beside the
         # headline, not as it.
         result["other_configs"] = {
-            str(k): time_config(kd, torch, workloads.CONFIGS[k](), steps=20, warmup=5)
+            str(k): time_config(kd, torch, workloads.CONFIGS[k](), steps=20, warmup=5,
+                                graph=k in (1, 2, 5))
             for k in (1, 2, 4, 5)
         }
         # Decode steps (one token per sequence) on the same channels.
         result["decode"] = {
             str(bsz): time_config(kd, torch, workloads.decode_batch(bsz), steps=20, warmup=5,
-                                  decode=True)
+                                  decode=True, graph=True)
             for bsz in (64, 256, 1024, 4096)
         }
         # Decode steps with the decode kernel page's operands: bf16 state, width-major weight.
         result["decode_bf16_state"] = {
             str(bsz): time_config(kd, torch, workloads.decode_batch_bf16_state(bsz), steps=20,
-                                  warmup=5)
-            for bsz in (1024, 4096)
+                                  warmup=5, graph=True)
+            for bsz in (64, 256, 1024, 4096)
         }
         # The same 16K-token workload with fp16 and FP32 x (output in x's format).
         result["other_formats"] = {
@@ -576,7 +613,8 @@ def main() -> int:
             sub = dataclasses.replace(wl, name=f"1 x {tokens} tokens, dim 4608, stride 9728",
                                       x=wl.x[:tokens],
                                       query_start_loc=np.array([0, tokens], dtype=np.int32))
-            result["context_sweep"][str(tokens)] = time_config(kd, torch, sub, steps=20, warmup=5)
+            result["context_sweep"][str(tokens)] = time_config(kd, torch, sub, steps=20, warmup=5,
+                                                               graph=True)
     if not args.no_cpu_baseline:
         configs = {k: (wl if k == 3 else workloads.CONFIGS[k]()) for k in (1, 2, 3, 4, 5)}
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_runs, configs)
