@@ -55,8 +55,35 @@ def _dtype_code(dtype: torch.dtype) -> int:
     return _DTYPE_CODES[dtype]
 
 
+# The current stream's raw handle: torch's direct query where it has one (0.1 us against
+# about 2 us for building a Stream object per call), else the public route.
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream_handle(device: torch.device) -> int:
+    if _raw_stream is not None:
+        idx = device.index if device.index is not None else torch.cuda.current_device()
+        return _raw_stream(idx)
     return torch.cuda.current_stream(device).cuda_stream
+
+
+class _NoGuard:
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        return False
+
+
+_NO_GUARD = _NoGuard()
+
+
+def _on(device: torch.device):
+    """The device context for a call on `device`: none when it is already current (the
+    context manager costs more than the launch's own host work)."""
+    if device.index is None or device.index == torch.cuda.current_device():
+        return _NO_GUARD
+    return torch.cuda.device(device)
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -88,9 +115,9 @@ def _check_common(x, weight, bias, conv_states, cache_indices, num_seqs):
     if x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be 2-D (tokens, dim) with unit column stride")
     dim = x.size(1)
-    if weight.dtype != torch.float32 or weight.dim() != 2 or tuple(weight.shape) != (dim, 4):
+    if weight.dtype != torch.float32 or weight.dim() != 2 or weight.shape != (dim, 4):
         raise ValueError("weight must be float32 of shape (dim, 4)")
-    if bias is not None and (bias.dtype != torch.float32 or tuple(bias.shape) != (dim,)
+    if bias is not None and (bias.dtype != torch.float32 or bias.shape != (dim,)
                              or not bias.is_contiguous()):
         raise ValueError("bias must be a contiguous float32 (dim,) tensor or None")
     if conv_states.dtype != torch.float32 or conv_states.dim() != 3 or conv_states.size(1) != dim:
@@ -99,8 +126,9 @@ def _check_common(x, weight, bias, conv_states, cache_indices, num_seqs):
         raise ValueError("conv_states needs at least 3 history entries per channel")
     if cache_indices.dtype != torch.int32 or cache_indices.dim() != 1 or cache_indices.numel() < num_seqs:
         raise ValueError("cache_indices must be a 1-D int32 tensor with one entry per sequence")
+    xi = x.get_device()
     for t in (weight, bias, conv_states, cache_indices):
-        if t is not None and t.device != x.device:
+        if t is not None and t.get_device() != xi:
             raise ValueError("all tensors must be on the device of x")
 
 
@@ -116,8 +144,9 @@ def _check_tensors(x, weight, bias, conv_states, query_start_loc, cache_indices,
             raise ValueError("has_initial_state must be a contiguous bool tensor or None")
         if has_initial_state.numel() < num_seqs:
             raise ValueError("has_initial_state needs one entry per sequence")
+    xi = x.get_device()
     for t in (query_start_loc, has_initial_state):
-        if t is not None and t.device != x.device:
+        if t is not None and t.get_device() != xi:
             raise ValueError("all tensors must be on the device of x")
 
 
@@ -154,7 +183,8 @@ def packed_causal_conv1d_fn(
     shape = (dim // part_dim, num_tokens, part_dim)
     if out is None:
         out = torch.empty(shape, dtype=x.dtype, device=x.device)
-    elif tuple(out.shape) != shape or out.dtype != x.dtype or not out.is_contiguous() or out.device != x.device:
+    elif (out.shape != shape or out.dtype != x.dtype or not out.is_contiguous()
+          or out.get_device() != x.get_device()):
         raise ValueError(f"out must be a contiguous {x.dtype} tensor of shape {shape} on {x.device}")
     # Nothing to convolve: return before touching anything (page: early return).
     if num_tokens == 0 or query_start_loc.numel() <= 1:
@@ -163,7 +193,7 @@ def packed_causal_conv1d_fn(
     lib = _lib.load()
     args = _conv_args(x, weight, bias, conv_states, query_start_loc, cache_indices,
                       has_initial_state, part_dim, activation, null_block_id, out)
-    with torch.cuda.device(x.device):
+    with _on(x.device):
         rc = lib.kdaconv_packed_causal_conv1d(*args, _stream_handle(x.device))
     _lib.check(rc, "packed_causal_conv1d_fn")
     return out
@@ -177,11 +207,11 @@ def _check_bf16_state(x, weight, bias, conv_states, cache_indices, batch, part_d
     dim = x.size(1)
     parts = dim // part_dim
     if weight.dtype != torch.float32 or not (
-            (weight.dim() == 2 and tuple(weight.shape) == (dim, 4))
-            or (weight.dim() == 3 and tuple(weight.shape) == (parts, 4, part_dim))):
+            (weight.dim() == 2 and weight.shape == (dim, 4))
+            or (weight.dim() == 3 and weight.shape == (parts, 4, part_dim))):
         raise ValueError("weight must be float32 (dim, 4) or width-major "
                          "(dim // part_dim, 4, part_dim)")
-    if bias is not None and (bias.dtype != torch.float32 or tuple(bias.shape) != (dim,)
+    if bias is not None and (bias.dtype != torch.float32 or bias.shape != (dim,)
                              or not bias.is_contiguous()):
         raise ValueError("bias must be a contiguous float32 (dim,) tensor or None")
     if conv_states.dim() != 3 or conv_states.size(1) != dim or conv_states.size(2) < 3:
@@ -190,8 +220,9 @@ def _check_bf16_state(x, weight, bias, conv_states, cache_indices, batch, part_d
         raise ValueError("cache_indices must be a 1-D int32 tensor with one entry per sequence")
     if not x.is_cuda:
         raise ValueError("x must be a GPU tensor")
+    xi = x.get_device()
     for t in (weight, bias, conv_states, cache_indices):
-        if t is not None and t.device != x.device:
+        if t is not None and t.get_device() != xi:
             raise ValueError("all tensors must be on the device of x")
 
 
@@ -236,7 +267,8 @@ def packed_causal_conv1d_update(
     shape = (dim // part_dim, batch, part_dim)
     if out is None:
         out = torch.empty(shape, dtype=x.dtype, device=x.device)
-    elif tuple(out.shape) != shape or out.dtype != x.dtype or not out.is_contiguous() or out.device != x.device:
+    elif (out.shape != shape or out.dtype != x.dtype or not out.is_contiguous()
+          or out.get_device() != x.get_device()):
         raise ValueError(f"out must be a contiguous {x.dtype} tensor of shape {shape} on {x.device}")
     if batch == 0:
         return out
@@ -252,7 +284,7 @@ def packed_causal_conv1d_update(
             _ptr(out), _stream_handle(x.device))
     states = (_ptr(conv_states), conv_states.size(0),
               conv_states.stride(0), conv_states.stride(1), conv_states.stride(2))
-    with torch.cuda.device(x.device):
+    with _on(x.device):
         if bf16_state:
             rc = lib.kdaconv_packed_causal_conv1d_update_bf16_state(
                 _ptr(x), _dtype_code(x.dtype), batch, dim, x.stride(0),
