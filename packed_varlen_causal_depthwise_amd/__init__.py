@@ -300,10 +300,10 @@ def packed_causal_conv1d_update(
 def packed_causal_conv1d_supported(x: torch.Tensor, weight: torch.Tensor,
                                    conv_states: torch.Tensor, part_dim: int) -> bool:
     """Whether packed_causal_conv1d_fn serves these tensors (page:
-    packed_causal_conv1d_supported). This build takes bf16, fp16 or FP32 x with
-    unit column stride and rows 16 bytes apart, FP32 weight (dim, 4), FP32
-    conv_states (lines, dim, >= 3) in any strided layout (entries 0..2 of the last
-    axis are the history), and part_dim a multiple of 8 dividing dim."""
+    packed_causal_conv1d_supported). The library takes bf16, fp16 or FP32 x with
+    unit column stride and any row stride (aligned to the element size), FP32 weight
+    (dim, 4), FP32 conv_states (lines, dim, >= 3) in any strided layout (entries 0..2
+    of the last axis are the history), and part_dim a multiple of 8 dividing dim."""
     try:
         if not (x.is_cuda and x.dim() == 2 and x.stride(1) == 1 and x.dtype in _DTYPE_CODES):
             return False
