@@ -63,7 +63,9 @@ def _weight(d, form: str) -> torch.Tensor:
     cm = wm.permute(0, 2, 1).reshape(-1, 4).contiguous()  # (dim, 4) [channel, width]
     if form == "channel_major":
         return cm
-    return cm.t().contiguous().t()  # (dim, 4) with strides (1, dim): scalar path
+    # (dim, 4) with strides (1, dim): part stride part_dim, channel stride 1, width stride
+    # dim, which the width-major vector path takes when part_dim and dim are multiples of 4
+    return cm.t().contiguous().t()
 
 
 def _run(d, weight=None, states=None, x=None):
@@ -211,3 +213,29 @@ def test_graph_replay():
         got = torch_to_words(out)
         assert np.array_equal(got, want), (rep, first_mismatches(got, want))
         assert np.array_equal(_state_words(st_view), ref_states), rep
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_fuzz(seed):
+    """Random batch sizes, part widths (partial column blocks), row pitches, null blocks,
+    lines outside the array, bias or none, SiLU or none, and weight and state forms."""
+    rng = np.random.default_rng(900 + seed)
+    pd = int(rng.choice([8, 16, 64, 72, 128, 192, 256, 520]))
+    batch = int(rng.integers(1, 700))
+    d = _case(batch, 3, pd, seed=910 + seed, lines=batch + int(rng.integers(1, 9)))
+    if rng.integers(2):
+        d.bias = None
+    if rng.integers(4) == 0:
+        d.activation = None
+    if rng.integers(2):
+        d.null_block_id = int(d.cache_indices[int(rng.integers(batch))])
+    if batch > 2 and rng.integers(2):
+        d.cache_indices[int(rng.integers(batch))] = -1
+    wform = ["width_major", "width_major_padded", "channel_major", "channel_major_transposed"][seed % 4]
+    sform = ["contiguous", "padded", "dim_first", "misaligned"][(seed // 2) % 4]
+    print(f"case: bf16-state fuzz seed {seed}: batch {batch} pd {pd} weight {wform} state {sform}",
+          flush=True)
+    got, st_view, _ = _run(d, weight=_weight(d, wform), states=_states16(d.conv_states, sform))
+    want, want_st = _want(d)
+    assert np.array_equal(got, want), first_mismatches(got, want)
+    assert np.array_equal(_state_words(st_view), want_st)

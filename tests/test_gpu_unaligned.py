@@ -166,3 +166,20 @@ def test_bf16_state_decode_unaligned():
                                                          d.cache_indices, 256, "silu", None)
     assert np.array_equal(got, want), first_mismatches(got, want)
     assert np.array_equal(torch_to_words(st_dev), st)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_fuzz_unaligned(seed):
+    """Seeded fuzz cases (zero-length sequences, null blocks, padding rows, several
+    part_dim values, wide accumulator ranges) with x at a random column offset of its
+    buffer and out at a random element offset, in every format."""
+    fmt = ["bf16", "f16", "f32"][seed % 3]
+    wl = workloads.random_case(3000 + seed, max_seqs=10, max_len=150, x_dtype=fmt,
+                               x_scale=[1.0, 8.0, 40.0][(seed // 3) % 3], pad_tokens=seed % 3)
+    rng = np.random.default_rng(seed)
+    off_x, off_o = int(rng.integers(1, 8)), int(rng.integers(1, 8))
+    print(f"case: {wl.name}, x at column {off_x}, out at element {off_o}", flush=True)
+    P = wl.dim // wl.part_dim
+    out = _out_at_offset((P, wl.num_tokens, wl.part_dim), TORCH_DTYPE[fmt], off_o)
+    got, st = _run(wl, _x_at_offset(wl, off_x), out=out)
+    _check(wl, got, st)
