@@ -210,7 +210,7 @@ def time_config(kd, torch, wl, steps: int, warmup: int, blocks: int = 10, decode
     one workload, with complete input/output/state sets rotated past the Infinity Cache.
     A ``workloads.Bf16StateDecode`` is timed as the decode step with its bf16 state and
     width-major weight. With x_column > 0, x is read from a buffer whose columns start that
-    many elements in (x not 16-byte aligned: the element-by-element path). With graph, the
+    many elements in (every lane's 8-byte vector of x unaligned). With graph, the
     same steps are also captured in a HIP graph and replayed (``graph``): for launches
     shorter than the binding's host time per call, the eager figure is the host's rate
     and the replayed one the GPU's."""
@@ -604,8 +604,8 @@ def main() -> int:
             fmt: time_config(kd, torch, workloads.config3(x_dtype=fmt), steps=20, warmup=5)
             for fmt in ("f16", "f32")
         }
-        # The headline workload with x read from column 1 of its buffer (not 16-byte
-        # aligned): the element-by-element path.
+        # The headline workload with x read from column 1 of its buffer: every lane's
+        # 8-byte vector of x starts 2 bytes past an 8-byte boundary.
         result["unaligned_x"] = time_config(kd, torch, wl, steps=20, warmup=5, x_column=1)
         # Context: one sequence of 2K-8K tokens (the first rows of the headline workload).
         result["context_sweep"] = {}

@@ -78,11 +78,11 @@ typedef enum kdaconv_dtype {
  *                    x[t * x_row_stride + c], rows t < num_tokens, channels c < dim.
  *                    Only columns [0, dim) are read. x_row_stride >= dim, any
  *                    value (page: unit column stride, any row stride). x must be
- *                    aligned to its element size (else EUNSUPPORTED). When x, out
- *                    and the row pitch are multiples of 8 bytes (bf16, fp16) or 16
- *                    bytes (FP32), 4 channels move as one vector; otherwise a slower
- *                    path moves them element by element (a Q|K|V slice at any column
- *                    offset).
+ *                    aligned to its element size (else EUNSUPPORTED). 4 channels
+ *                    move as one vector whatever the alignment, so a Q|K|V slice
+ *                    may start at any column; vectors at addresses that are not
+ *                    multiples of 8 bytes (bf16, fp16) or 16 bytes (FP32) cost
+ *                    some speed.
  * dtype              KDACONV_BF16, KDACONV_F16 or KDACONV_F32 (else EINVAL): the
  *                    format of x and of out.
  * weight             FP32; tap k of channel c at weight[c * weight_stride0 +

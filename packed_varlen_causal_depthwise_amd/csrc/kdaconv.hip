@@ -87,7 +87,12 @@ constexpr int rows_per_tile() {
 
 int rows_per_tile(int dtype) { return dtype == kF32 ? rows_per_tile<kF32>() : rows_per_tile<kBF16>(); }
 
-// Buffer loads and stores of kBytes per lane.
+// Buffer loads and stores of kBytes per lane. A lane's vector may start at any element
+// of x or out (a Q|K|V slice at any column, rows any number of elements apart): queues of
+// the HSA runtime on gfx9-family GPUs run with unaligned vector memory access enabled,
+// which the compiler's own code for the amdhsa target also relies on (it moves
+// unaligned copies with 8-byte loads and stores). Vectors that are not naturally aligned
+// cost some speed, not correctness.
 template <int kBytes>
 struct Lane;
 
@@ -116,49 +121,6 @@ struct Lane<16> {
   static __device__ __forceinline__ void store(vec v, __amdgpu_buffer_rsrc_t r, uint32_t vo,
                                                uint32_t so) {
     __builtin_amdgcn_raw_buffer_store_b128(v, r, vo, so, kPolicy);
-  }
-};
-
-typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-
-// The same per-lane vectors moved one element at a time, for x and out that are not
-// aligned to the vector (a Q|K|V slice at any column offset, any row stride): 2-byte
-// loads and stores for bf16 and fp16, 4-byte ones for FP32. Pairs of 2-byte loads
-// fill the two halves of a word, which the compiler does without waiting for them.
-template <int kF, int V>
-struct LaneElems {
-  static constexpr int kB = element_bytes<kF>();
-  typedef typename Lane<V * kB>::vec vec;
-  template <int kPolicy>
-  static __device__ __forceinline__ vec load(__amdgpu_buffer_rsrc_t r, uint32_t vo, uint32_t so) {
-    vec v;
-    if (kB == 4) {
-#pragma unroll
-      for (int i = 0; i < V; ++i) v[i] = __builtin_amdgcn_raw_buffer_load_b32(r, vo + 4u * i, so, kPolicy);
-    } else {
-#pragma unroll
-      for (int i = 0; i < V / 2; ++i) {
-        u16x2 h;
-        h[0] = __builtin_amdgcn_raw_buffer_load_b16(r, vo + 4u * i, so, kPolicy);
-        h[1] = __builtin_amdgcn_raw_buffer_load_b16(r, vo + 4u * i + 2u, so, kPolicy);
-        v[i] = __builtin_bit_cast(uint32_t, h);
-      }
-    }
-    return v;
-  }
-  template <int kPolicy>
-  static __device__ __forceinline__ void store(vec v, __amdgpu_buffer_rsrc_t r, uint32_t vo,
-                                               uint32_t so) {
-    if (kB == 4) {
-#pragma unroll
-      for (int i = 0; i < V; ++i) __builtin_amdgcn_raw_buffer_store_b32(v[i], r, vo + 4u * i, so, kPolicy);
-    } else {
-#pragma unroll
-      for (int i = 0; i < V / 2; ++i) {
-        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(v[i] & 0xFFFFu), r, vo + 4u * i, so, kPolicy);
-        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(v[i] >> 16), r, vo + 4u * i + 2u, so, kPolicy);
-      }
-    }
   }
 };
 
@@ -207,7 +169,6 @@ struct ConvParams {
   int32_t bias_vec;  // bias is 16-byte aligned
   int32_t state_vec;  // each state line is (dim, 3) contiguous and 16-byte aligned
                       // (bf16 state: 8-byte aligned)
-  int32_t xo_vec;  // x, out and the x row pitch aligned to the lane's vector
   int32_t state_rows;  // each state line is 3 rows of dim contiguous channels ("dim first"),
                        // 16-byte aligned, row and line strides multiples of 4
 };
@@ -433,12 +394,11 @@ __device__ __forceinline__ Tile describe_tile(const ConvParams& P, int p, int la
 // The per-wave part of the convolution shared by the prefill and decode kernels:
 // the lane's channels, its weights and bias, the state line's I/O, prefill tiles
 // and decode steps.
-template <int kF, int V, int R, bool kBias, bool kSilu, int kS = kStateF32, bool kA = true>
+template <int kF, int V, int R, bool kBias, bool kSilu, int kS = kStateF32>
 struct ConvWorker {
   static constexpr int kBytes = element_bytes<kF>();
-  // kA: x, out and the x row pitch are aligned to the lane's vector of V elements, which
-  // moves as one load or store per row; otherwise element by element.
-  typedef typename std::conditional<kA, Lane<V * kBytes>, LaneElems<kF, V>>::type L;
+  // A lane's V elements of a row of x or out move as one load or store.
+  typedef Lane<V * kBytes> L;
   typedef typename L::vec vec;
 
   const ConvParams& P;
@@ -1079,7 +1039,7 @@ struct ConvWorker {
 // kG adjacent column blocks (a column group). wave_slot maps the one-dimensional
 // launch to programs and column groups so that workgroups dispatched together cover
 // whole rows.
-template <int kF, int V, int R, int kG, bool kBias, bool kSilu, bool kA>
+template <int kF, int V, int R, int kG, bool kBias, bool kSilu>
 __global__ __launch_bounds__(kWave * kG) __attribute__((amdgpu_waves_per_eu(kMinWaves))) void packed_conv_kernel(const ConvParams P) {
   static_assert(V % 4 == 0, "the vector weight, bias and state paths take 4 channels at a time");
   const int lane = threadIdx.x % kWave;
@@ -1091,7 +1051,7 @@ __global__ __launch_bounds__(kWave * kG) __attribute__((amdgpu_waves_per_eu(kMin
   // Weights first: their loads overlap the search for the tile's sequence.
   __shared__ uint2 fix_slots[kG][kFixCapacity];
   __shared__ float stage[kG][3 * V * kWave];
-  ConvWorker<kF, V, R, kBias, kSilu, kStateF32, kA> w(P, lane, cb, fix_slots[wave], stage[wave]);
+  ConvWorker<kF, V, R, kBias, kSilu, kStateF32> w(P, lane, cb, fix_slots[wave], stage[wave]);
   w.load_weights();
   const Tile d = describe_tile<R>(P, p, lane);
   if (!d.valid) return;
@@ -1123,7 +1083,7 @@ __global__ __launch_bounds__(kWave * kG) __attribute__((amdgpu_waves_per_eu(kMin
 // Decode update: program p is sequences kSeq p .. kSeq p + kSeq - 1 (rows of x), one
 // wave per column block, kG column blocks per workgroup. No search: every sequence
 // has exactly one token.
-template <int kF, int V, int kSeq, int kG, bool kBias, bool kSilu, int kS, bool kA>
+template <int kF, int V, int kSeq, int kG, bool kBias, bool kSilu, int kS>
 __global__ __launch_bounds__(kWave * kG) void packed_conv_update_kernel(const ConvParams P) {
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
@@ -1132,7 +1092,7 @@ __global__ __launch_bounds__(kWave * kG) void packed_conv_update_kernel(const Co
   const int cb = slot.cb;
   if (cb >= P.col_blocks) return;
   __shared__ float stage[kG][3 * V * kWave];
-  ConvWorker<kF, V, 1, kBias, kSilu, kS, kA> w(P, lane, cb, nullptr, stage[wave]);
+  ConvWorker<kF, V, 1, kBias, kSilu, kS> w(P, lane, cb, nullptr, stage[wave]);
   w.load_weights();
   if (P.state_vec)
     w.template decode_many<kSeq, true>(p * kSeq);
@@ -1191,15 +1151,6 @@ bool aligned8(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0
 bool element_aligned(const void* p, int64_t eb) {
   return (reinterpret_cast<uintptr_t>(p) & (uintptr_t)(eb - 1)) == 0;
 }
-// x and out take the vector path when every lane's vector (4 elements: 8 bytes for bf16
-// and fp16, 16 for FP32) is naturally aligned: x, out and the x row pitch are multiples
-// of the vector size.
-bool vector_io(const void* x, int64_t x_row_stride, int64_t eb, const void* out) {
-  const uintptr_t vb = (uintptr_t)(kLaneChannels * eb);
-  return (reinterpret_cast<uintptr_t>(x) % vb) == 0 && (reinterpret_cast<uintptr_t>(out) % vb) == 0 &&
-         (x_row_stride * eb) % (int64_t)vb == 0;
-}
-
 bool known_dtype(int dtype) { return dtype == kBF16 || dtype == kF16 || dtype == kF32; }
 
 int64_t dtype_bytes(int dtype) { return dtype == kF32 ? 4 : 2; }
@@ -1215,7 +1166,8 @@ int validate(const void* x, int dtype, int64_t num_tokens, int64_t dim, int64_t 
   if (x_row_stride < dim) return KDACONV_EINVAL;
   if (activation != KDACONV_ACT_NONE && activation != KDACONV_ACT_SILU) return KDACONV_EINVAL;
   const int64_t eb = dtype_bytes(dtype);
-  // Plane rows are whole 16-byte pieces (x and its rows may be unaligned: element path).
+  // Plane rows are whole 16-byte pieces (x, out and x's rows need only be aligned to the
+  // element size).
   if (part_dim % 8 != 0) return KDACONV_EUNSUPPORTED;
   if (ws0 < 0 || ws1 < 0 || cs0 < 0 || cs1 < 0 || cs2 < 0 || ci_stride < 0)
     return KDACONV_EUNSUPPORTED;
@@ -1262,7 +1214,7 @@ int validate_update(const void* x, int dtype, int64_t batch, int64_t dim, int64_
   return KDACONV_OK;
 }
 
-template <int kF, int V, int kG, bool kA>
+template <int kF, int V, int kG>
 void launch_group(ConvParams P, bool bias, bool silu, hipStream_t st) {
   constexpr int R = rows_per_tile<kF>();
   const uint64_t groups = ((uint64_t)P.col_blocks + kG - 1) / kG;
@@ -1271,14 +1223,14 @@ void launch_group(ConvParams P, bool bias, bool silu, hipStream_t st) {
   const dim3 block(kWave * kG);
   if (bias) {
     if (silu)
-      hipLaunchKernelGGL((packed_conv_kernel<kF, V, R, kG, true, true, kA>), grid, block, 0, st, P);
+      hipLaunchKernelGGL((packed_conv_kernel<kF, V, R, kG, true, true>), grid, block, 0, st, P);
     else
-      hipLaunchKernelGGL((packed_conv_kernel<kF, V, R, kG, true, false, kA>), grid, block, 0, st, P);
+      hipLaunchKernelGGL((packed_conv_kernel<kF, V, R, kG, true, false>), grid, block, 0, st, P);
   } else {
     if (silu)
-      hipLaunchKernelGGL((packed_conv_kernel<kF, V, R, kG, false, true, kA>), grid, block, 0, st, P);
+      hipLaunchKernelGGL((packed_conv_kernel<kF, V, R, kG, false, true>), grid, block, 0, st, P);
     else
-      hipLaunchKernelGGL((packed_conv_kernel<kF, V, R, kG, false, false, kA>), grid, block, 0, st, P);
+      hipLaunchKernelGGL((packed_conv_kernel<kF, V, R, kG, false, false>), grid, block, 0, st, P);
   }
 }
 
@@ -1299,16 +1251,13 @@ void launch(ConvParams P, int64_t cols, bool bias, bool silu, hipStream_t st) {
   // Two waves per workgroup measured 3-4 % faster on the 16384 x 4608 bf16
   // workload; with an odd number of column blocks the second wave of every last
   // workgroup would idle, and one wave per workgroup is kept.
-  // Unaligned x or out (element loads and stores) take one wave per workgroup only.
-  if (!P.xo_vec)
-    launch_group<kF, V, 1, false>(P, bias, silu, st);
-  else if (P.col_blocks % 2 == 0)
-    launch_group<kF, V, 2, true>(P, bias, silu, st);
+  if (P.col_blocks % 2 == 0)
+    launch_group<kF, V, 2>(P, bias, silu, st);
   else
-    launch_group<kF, V, 1, true>(P, bias, silu, st);
+    launch_group<kF, V, 1>(P, bias, silu, st);
 }
 
-template <int kF, int V, int kSeq, int kG, int kS, bool kA>
+template <int kF, int V, int kSeq, int kG, int kS>
 void launch_update_group(ConvParams P, bool bias, bool silu, hipStream_t st) {
   const uint64_t groups = ((uint64_t)P.col_blocks + kG - 1) / kG;
   set_wave_order(P, groups, false);
@@ -1316,27 +1265,24 @@ void launch_update_group(ConvParams P, bool bias, bool silu, hipStream_t st) {
   const dim3 block(kWave * kG);
   if (bias) {
     if (silu)
-      hipLaunchKernelGGL((packed_conv_update_kernel<kF, V, kSeq, kG, true, true, kS, kA>), grid, block, 0, st, P);
+      hipLaunchKernelGGL((packed_conv_update_kernel<kF, V, kSeq, kG, true, true, kS>), grid, block, 0, st, P);
     else
-      hipLaunchKernelGGL((packed_conv_update_kernel<kF, V, kSeq, kG, true, false, kS, kA>), grid, block, 0, st, P);
+      hipLaunchKernelGGL((packed_conv_update_kernel<kF, V, kSeq, kG, true, false, kS>), grid, block, 0, st, P);
   } else {
     if (silu)
-      hipLaunchKernelGGL((packed_conv_update_kernel<kF, V, kSeq, kG, false, true, kS, kA>), grid, block, 0, st, P);
+      hipLaunchKernelGGL((packed_conv_update_kernel<kF, V, kSeq, kG, false, true, kS>), grid, block, 0, st, P);
     else
-      hipLaunchKernelGGL((packed_conv_update_kernel<kF, V, kSeq, kG, false, false, kS, kA>), grid, block, 0, st, P);
+      hipLaunchKernelGGL((packed_conv_update_kernel<kF, V, kSeq, kG, false, false, kS>), grid, block, 0, st, P);
   }
 }
 
-template <int kF, int V, int kSeq, int kS, bool kA>
+template <int kF, int V, int kSeq, int kS>
 void launch_update_seq(ConvParams P, bool bias, bool silu, hipStream_t st) {
   P.programs = (P.num_seqs + kSeq - 1) / kSeq;
-  if constexpr (kA) {
-    if (P.col_blocks % 2 == 0) {
-      launch_update_group<kF, V, kSeq, 2, kS, true>(P, bias, silu, st);
-      return;
-    }
-  }
-  launch_update_group<kF, V, kSeq, 1, kS, kA>(P, bias, silu, st);
+  if (P.col_blocks % 2 == 0)
+    launch_update_group<kF, V, kSeq, 2, kS>(P, bias, silu, st);
+  else
+    launch_update_group<kF, V, kSeq, 1, kS>(P, bias, silu, st);
 }
 
 // Sequences per decode wave: as many as keep at least 2048 waves in the launch (two per
@@ -1348,16 +1294,12 @@ template <int kF, int V, int kS = kStateF32>
 void launch_update(ConvParams P, int64_t cols, bool bias, bool silu, hipStream_t st) {
   P.col_blocks = (int32_t)((cols / V + kWave - 1) / kWave);
   const int64_t waves1 = (int64_t)P.num_seqs * P.col_blocks;
-  // Unaligned x or out (element loads and stores): one sequence per wave, one wave per
-  // workgroup.
-  if (!P.xo_vec)
-    launch_update_seq<kF, V, 1, kS, false>(P, bias, silu, st);
-  else if (waves1 >= 4 * 2048)
-    launch_update_seq<kF, V, 4, kS, true>(P, bias, silu, st);
+  if (waves1 >= 4 * 2048)
+    launch_update_seq<kF, V, 4, kS>(P, bias, silu, st);
   else if (waves1 >= 2 * 2048)
-    launch_update_seq<kF, V, 2, kS, true>(P, bias, silu, st);
+    launch_update_seq<kF, V, 2, kS>(P, bias, silu, st);
   else
-    launch_update_seq<kF, V, 1, kS, true>(P, bias, silu, st);
+    launch_update_seq<kF, V, 1, kS>(P, bias, silu, st);
 }
 
 // Fields of ConvParams shared by both operations.
@@ -1471,7 +1413,6 @@ extern "C" int kdaconv_packed_causal_conv1d(
   P.qsl = query_start_loc;
   P.has_init = has_initial_state;
   P.num_seqs = (int32_t)num_seqs;
-  P.xo_vec = vector_io(x, x_row_stride, eb, out);
   int levels = 0;
   int64_t reach = 1;
   while (reach < num_seqs) {
@@ -1514,7 +1455,6 @@ extern "C" int kdaconv_packed_causal_conv1d_update(
               conv_states, num_cache_lines, cs_stride0, cs_stride1, cs_stride2, cache_indices,
               cache_indices_stride, dim, part_dim, has_null_block, null_block_id);
   P.num_seqs = (int32_t)batch;
-  P.xo_vec = vector_io(x, x_row_stride, eb, out);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const bool silu = activation == KDACONV_ACT_SILU;
   const bool has_bias = bias != nullptr;
@@ -1550,7 +1490,6 @@ extern "C" int kdaconv_packed_causal_conv1d_update_bf16_state(
               cs_stride2, cache_indices, cache_indices_stride, dim, part_dim, has_null_block,
               null_block_id);
   P.num_seqs = (int32_t)batch;
-  P.xo_vec = vector_io(x, x_row_stride, 2, out);
   P.w_part_stride = weight_part_stride;
   const int64_t parts = dim / part_dim;
   const int64_t w_extent = (parts - 1) * weight_part_stride + part_dim + 3 * weight_stride1;

@@ -68,8 +68,8 @@ def _args(**kw):
     (dict(b=0), _lib.OK),  # no bias
     (dict(init=0), _lib.OK),  # no initial states
     (dict(dim=96, sx=96, pd=12), _lib.EUNSUPPORTED),  # part_dim not a multiple of 8
-    (dict(sx=390), _lib.OK),  # rows not 16 bytes apart: element path
-    (dict(x=A + 2), _lib.OK),  # x at an odd column: element path
+    (dict(sx=390), _lib.OK),  # rows not 16 bytes apart: unaligned vectors
+    (dict(x=A + 2), _lib.OK),  # x at an odd column: unaligned vectors
     (dict(out=A + 8), _lib.OK),
     (dict(x=A + 1), _lib.EUNSUPPORTED),  # not aligned to the element size
     (dict(out=A + 1), _lib.EUNSUPPORTED),
@@ -83,7 +83,7 @@ def _args(**kw):
     (dict(dt=-1), _lib.EINVAL),
     (dict(dt=_lib.F16), _lib.OK),
     (dict(dt=_lib.F32), _lib.OK),
-    (dict(dt=_lib.F16, sx=388), _lib.OK),  # fp16 rows 776 bytes apart: element path
+    (dict(dt=_lib.F16, sx=388), _lib.OK),  # fp16 rows 776 bytes apart: unaligned vectors
     (dict(dt=_lib.F32, sx=388), _lib.OK),  # FP32 rows 1552 bytes apart
     (dict(dt=_lib.F32, sx=386), _lib.OK),
     (dict(dt=_lib.F32, T=1 << 25, pd=8, dim=8, sx=8), _lib.EUNSUPPORTED),  # plane of 2^30 bytes

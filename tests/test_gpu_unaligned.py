@@ -2,8 +2,9 @@
 
 Page vllm.models.kimi_k3.nvidia.ops.kda_conv, packed_causal_conv1d_supported: x needs a
 unit column stride and may have any row stride, so a Q|K|V slice may start at any
-column of the in_proj output. Such x (and an out at any element offset) take the
-element-by-element path of the kernels. Each case compares outputs and states with the
+column of the in_proj output. Such x (and an out at any element offset) move through
+the same 8- and 16-byte lane vectors as aligned ones, at addresses that are not
+multiples of the vector size. Each case compares outputs and states with the
 oracle word for word: ragged sequences over several tiles, every format, odd row
 strides, the exact-SiLU path, the decode step with either state, and the 16384-token
 workload read from a slice at column 1.
@@ -76,9 +77,8 @@ def _case(fmt, seed, x_scale=1.0, act="silu", row_stride=3 * 200 + 9):
                          null_block_id=None)
 
 
-# Offsets that are a multiple of 4 elements keep 2-byte formats on the vector path (8-byte
-# vectors); the others, and every FP32 offset that is not a multiple of 4, take the
-# element path.
+# Offsets that are a multiple of 4 elements keep 2-byte formats' 8-byte vectors aligned;
+# the others, and every FP32 offset that is not a multiple of 4, make them unaligned.
 @pytest.mark.parametrize("fmt,off", [("bf16", 1), ("bf16", 3), ("bf16", 4), ("bf16", 5),
                                      ("f16", 1), ("f16", 4), ("f16", 7), ("f32", 1), ("f32", 2),
                                      ("f32", 3)])
