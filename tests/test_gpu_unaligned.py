@@ -183,3 +183,51 @@ def test_fuzz_unaligned(seed):
     out = _out_at_offset((P, wl.num_tokens, wl.part_dim), TORCH_DTYPE[fmt], off_o)
     got, st = _run(wl, _x_at_offset(wl, off_x), out=out)
     _check(wl, got, st)
+
+
+@pytest.mark.parametrize("batch", [300, 600])
+@pytest.mark.parametrize("fmt", ["bf16", "f16", "f32"])
+def test_decode_unaligned_several_per_wave(fmt, batch):
+    """Batches that give two (300) and four (600) sequences per wave at dim 4608 (18 column
+    blocks, two waves per workgroup), x at column 3 of rows 9731 elements apart and out at
+    element 1."""
+    wl = workloads.decode_batch(batch, seed=240 + batch, x_dtype=fmt)
+    print(f"case: decode, {batch} sequences, x at column 3, out at element 1, {fmt}", flush=True)
+    x = _x_at_offset(wl, 3)
+    out = _out_at_offset((3, batch, 1536), TORCH_DTYPE[fmt], 1)
+    st_dev = torch.from_numpy(wl.conv_states.copy()).cuda()
+    kd.packed_causal_conv1d_update(x, torch.from_numpy(wl.weight).cuda(),
+                                   torch.from_numpy(wl.bias).cuda(), st_dev,
+                                   torch.from_numpy(wl.cache_indices).cuda(), 1536, "silu", None,
+                                   out=out)
+    torch.cuda.synchronize()
+    got = torch_to_words(out)
+    st = wl.conv_states.copy()
+    want = oracle.packed_causal_conv1d_update(wl.x, wl.dim, wl.weight, wl.bias, st,
+                                              wl.cache_indices, 1536, "silu", None, x_dtype=fmt)
+    assert np.array_equal(got, want), first_mismatches(got, want)
+    assert np.array_equal(st_dev.cpu().numpy().view(np.uint32), st.view(np.uint32))
+
+
+@pytest.mark.parametrize("batch", [300, 600])
+def test_bf16_state_decode_unaligned_several_per_wave(batch):
+    d = workloads.decode_batch_bf16_state(batch, seed=250 + batch)
+    print(f"case: bf16-state decode, {batch} sequences, x at column 1, out at element 3",
+          flush=True)
+    T, rs = d.x.shape
+    buf = np.zeros((T, rs + 1), dtype=np.uint16)
+    buf[:, 1:] = d.x
+    x = words_to_torch(buf, torch.bfloat16)[:, 1:1 + d.dim]
+    out = _out_at_offset((3, batch, 1536), torch.bfloat16, 3)
+    st_dev = torch.from_numpy(d.conv_states.view(np.int16).copy()).cuda().view(torch.bfloat16)
+    kd.packed_causal_conv1d_update(x, torch.from_numpy(d.weight).cuda(),
+                                   torch.from_numpy(d.bias).cuda(), st_dev,
+                                   torch.from_numpy(d.cache_indices).cuda(), 1536, "silu", None,
+                                   out=out)
+    torch.cuda.synchronize()
+    got = torch_to_words(out)
+    st = d.conv_states.copy()
+    want = oracle.packed_causal_conv1d_update_bf16_state(d.x, d.dim, d.weight, d.bias, st,
+                                                         d.cache_indices, 1536, "silu", None)
+    assert np.array_equal(got, want), first_mismatches(got, want)
+    assert np.array_equal(torch_to_words(st_dev), st)
