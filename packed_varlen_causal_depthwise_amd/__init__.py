@@ -58,11 +58,18 @@ def _dtype_code(dtype: torch.dtype) -> int:
 # The current stream's raw handle: torch's direct query where it has one (0.1 us against
 # about 2 us for building a Stream object per call), else the public route.
 _raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+# The current device, likewise by the direct query where torch has one (a plain call,
+# without the initialisation checks of torch.cuda.current_device()).
+_get_device = getattr(torch._C, "_cuda_getDevice", None)
+
+
+def _current_device() -> int:
+    return _get_device() if _get_device is not None else torch.cuda.current_device()
 
 
 def _stream_handle(device: torch.device) -> int:
     if _raw_stream is not None:
-        idx = device.index if device.index is not None else torch.cuda.current_device()
+        idx = device.index if device.index is not None else _current_device()
         return _raw_stream(idx)
     return torch.cuda.current_stream(device).cuda_stream
 
@@ -81,7 +88,7 @@ _NO_GUARD = _NoGuard()
 def _on(device: torch.device):
     """The device context for a call on `device`: none when it is already current (the
     context manager costs more than the launch's own host work)."""
-    if device.index is None or device.index == torch.cuda.current_device():
+    if device.index is None or device.index == _current_device():
         return _NO_GUARD
     return torch.cuda.device(device)
 
@@ -90,17 +97,20 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else t.data_ptr()
 
 
+# Shapes and strides are read as whole tuples, once per tensor: torch's t.stride(i) and
+# t.size(i) each cost two to three times t.stride() or t.shape.
 def _conv_args(x, weight, bias, conv_states, query_start_loc, cache_indices, has_initial_state,
                part_dim, activation, null_block_id, out):
     num_tokens, dim = x.shape
     num_seqs = query_start_loc.numel() - 1
+    ws = weight.stride()
+    cs = conv_states.stride()
     return [
-        _ptr(x), _dtype_code(x.dtype), num_tokens, dim, x.stride(0),
-        _ptr(weight), weight.stride(0), weight.stride(1), _ptr(bias),
-        _ptr(conv_states), conv_states.size(0),
-        conv_states.stride(0), conv_states.stride(1), conv_states.stride(2),
+        _ptr(x), _dtype_code(x.dtype), num_tokens, dim, x.stride()[0],
+        _ptr(weight), ws[0], ws[1], _ptr(bias),
+        _ptr(conv_states), conv_states.shape[0], cs[0], cs[1], cs[2],
         _ptr(query_start_loc), num_seqs,
-        _ptr(cache_indices), cache_indices.stride(0) if cache_indices.dim() == 1 else 0,
+        _ptr(cache_indices), cache_indices.stride()[0] if cache_indices.dim() == 1 else 0,
         _ptr(has_initial_state),
         int(part_dim), _activation_code(activation),
         int(null_block_id is not None), 0 if null_block_id is None else int(null_block_id),
@@ -112,17 +122,18 @@ def _check_common(x, weight, bias, conv_states, cache_indices, num_seqs):
     if not x.is_cuda:
         raise ValueError("x must be a GPU tensor")
     _dtype_code(x.dtype)
-    if x.dim() != 2 or x.stride(1) != 1:
+    if x.dim() != 2 or x.stride()[1] != 1:
         raise ValueError("x must be 2-D (tokens, dim) with unit column stride")
-    dim = x.size(1)
+    dim = x.shape[1]
     if weight.dtype != torch.float32 or weight.dim() != 2 or weight.shape != (dim, 4):
         raise ValueError("weight must be float32 of shape (dim, 4)")
     if bias is not None and (bias.dtype != torch.float32 or bias.shape != (dim,)
                              or not bias.is_contiguous()):
         raise ValueError("bias must be a contiguous float32 (dim,) tensor or None")
-    if conv_states.dtype != torch.float32 or conv_states.dim() != 3 or conv_states.size(1) != dim:
+    cshape = conv_states.shape
+    if conv_states.dtype != torch.float32 or len(cshape) != 3 or cshape[1] != dim:
         raise ValueError("conv_states must be float32 of shape (cache lines, dim, >= 3)")
-    if conv_states.size(2) < 3:
+    if cshape[2] < 3:
         raise ValueError("conv_states needs at least 3 history entries per channel")
     if cache_indices.dtype != torch.int32 or cache_indices.dim() != 1 or cache_indices.numel() < num_seqs:
         raise ValueError("cache_indices must be a 1-D int32 tensor with one entry per sequence")
@@ -202,9 +213,9 @@ def packed_causal_conv1d_fn(
 def _check_bf16_state(x, weight, bias, conv_states, cache_indices, batch, part_dim):
     if x.dtype != torch.bfloat16:
         raise ValueError("a bf16 conv state takes bf16 x (page: is_fused_kda_decode_supported)")
-    if x.dim() != 2 or x.stride(1) != 1:
+    if x.dim() != 2 or x.stride()[1] != 1:
         raise ValueError("x must be 2-D (batch, dim) with unit column stride")
-    dim = x.size(1)
+    dim = x.shape[1]
     parts = dim // part_dim
     if weight.dtype != torch.float32 or not (
             (weight.dim() == 2 and weight.shape == (dim, 4))
@@ -214,7 +225,8 @@ def _check_bf16_state(x, weight, bias, conv_states, cache_indices, batch, part_d
     if bias is not None and (bias.dtype != torch.float32 or bias.shape != (dim,)
                              or not bias.is_contiguous()):
         raise ValueError("bias must be a contiguous float32 (dim,) tensor or None")
-    if conv_states.dim() != 3 or conv_states.size(1) != dim or conv_states.size(2) < 3:
+    cshape = conv_states.shape
+    if len(cshape) != 3 or cshape[1] != dim or cshape[2] < 3:
         raise ValueError("conv_states must be bf16 of shape (cache lines, dim, >= 3)")
     if cache_indices.dtype != torch.int32 or cache_indices.dim() != 1 or cache_indices.numel() < batch:
         raise ValueError("cache_indices must be a 1-D int32 tensor with one entry per sequence")
@@ -229,9 +241,10 @@ def _check_bf16_state(x, weight, bias, conv_states, cache_indices, batch, part_d
 def _weight_strides(weight: torch.Tensor, part_dim: int):
     """(part stride, channel stride, width stride) of a (dim, 4) or a width-major
     (dim // part_dim, 4, part_dim) weight, in elements."""
-    if weight.dim() == 2:
-        return part_dim * weight.stride(0), weight.stride(0), weight.stride(1)
-    return weight.stride(0), weight.stride(2), weight.stride(1)
+    ws = weight.stride()
+    if len(ws) == 2:
+        return part_dim * ws[0], ws[0], ws[1]
+    return ws[0], ws[2], ws[1]
 
 
 def packed_causal_conv1d_update(
@@ -278,21 +291,23 @@ def packed_causal_conv1d_update(
     else:
         _check_common(x, weight, bias, conv_states, cache_indices, batch)
     lib = _lib.load()
-    tail = (_ptr(cache_indices), cache_indices.stride(0),
+    tail = (_ptr(cache_indices), cache_indices.stride()[0],
             int(part_dim), _activation_code(activation),
             int(null_block_id is not None), 0 if null_block_id is None else int(null_block_id),
             _ptr(out), _stream_handle(x.device))
-    states = (_ptr(conv_states), conv_states.size(0),
-              conv_states.stride(0), conv_states.stride(1), conv_states.stride(2))
+    cs = conv_states.stride()
+    states = (_ptr(conv_states), conv_states.shape[0], cs[0], cs[1], cs[2])
+    x_row_stride = x.stride()[0]
     with _on(x.device):
         if bf16_state:
             rc = lib.kdaconv_packed_causal_conv1d_update_bf16_state(
-                _ptr(x), _dtype_code(x.dtype), batch, dim, x.stride(0),
+                _ptr(x), _dtype_code(x.dtype), batch, dim, x_row_stride,
                 _ptr(weight), *_weight_strides(weight, part_dim), _ptr(bias), *states, *tail)
         else:
+            ws = weight.stride()
             rc = lib.kdaconv_packed_causal_conv1d_update(
-                _ptr(x), _dtype_code(x.dtype), batch, dim, x.stride(0),
-                _ptr(weight), weight.stride(0), weight.stride(1), _ptr(bias), *states, *tail)
+                _ptr(x), _dtype_code(x.dtype), batch, dim, x_row_stride,
+                _ptr(weight), ws[0], ws[1], _ptr(bias), *states, *tail)
     _lib.check(rc, "packed_causal_conv1d_update")
     return out
 
