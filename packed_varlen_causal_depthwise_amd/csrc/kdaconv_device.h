@@ -107,11 +107,12 @@ __device__ __forceinline__ uint32_t word_exact(float y) {
 //   silu_bound<kF>()      bound on the error where the fast path is trusted
 //   exact_below<kF>()     accumulators below it take the exact path
 //   fast_exp_limit<kF>()  row test for them: every a below exact_below has an exp2
-//                         result at or above this bit pattern (2048.0f: a < -7.6;
-//                         32.0f: a < -3.46), so a row whose largest exp2 result is
-//                         smaller holds none. NaN of either sign also lies above it:
-//                         exp2 never returns a negative number and every NaN
-//                         pattern is larger.
+//                         result at or above this bit pattern (1800.0f, under the
+//                         1808.04 that a = -7.5 gives; 54.5f, under the 54.598 of
+//                         a = -4; both far beyond the exp2 error), so a row whose
+//                         largest exp2 result is smaller holds none. NaN of either
+//                         sign also lies above it: exp2 never returns a negative
+//                         number and every NaN pattern is larger.
 template <int kF>
 constexpr uint32_t silu_bound() {
   return kF == kF16 ? 6u : 10u;
@@ -122,7 +123,7 @@ constexpr float exact_below() {
 }
 template <int kF>
 constexpr uint32_t fast_exp_limit() {
-  return kF == kF16 ? 0x42000000u : 0x45000000u;
+  return kF == kF16 ? 0x425A0000u : 0x44E10000u;
 }
 
 // SiLU from the hardware exp2 and reciprocal; e receives the exp2 result, which
