@@ -195,7 +195,8 @@ def packed_causal_conv1d(x: np.ndarray, dim: int, weight: np.ndarray, bias: Opti
     lib = lib or load()
     wd = WORD_DTYPE[x_dtype]
     esize = np.dtype(wd).itemsize
-    assert x.dtype == wd and x.ndim == 2 and x.strides[1] == esize
+    # unit column stride (numpy gives an empty array zero strides: no rows, nothing read)
+    assert x.dtype == wd and x.ndim == 2 and (x.strides[1] == esize or x.shape[0] == 0)
     assert weight.dtype == np.float32 and weight.ndim == 2 and weight.shape == (dim, 4)
     assert conv_states.dtype == np.float32 and conv_states.ndim == 3
     # The state is entries 0..2 of the last axis; wider states keep the rest untouched.
@@ -213,8 +214,9 @@ def packed_causal_conv1d(x: np.ndarray, dim: int, weight: np.ndarray, bias: Opti
     assert out.dtype == wd and out.flags.c_contiguous
     assert out.shape == (dim // part_dim, T, part_dim)
     S = qsl.shape[0] - 1
+    row_stride = x.strides[0] // esize if T else x.shape[1]  # no rows: the pitch is unused
     rc = lib.oracle_packed_causal_conv1d(
-        x.ctypes.data, FORMATS[x_dtype], T, dim, x.strides[0] // esize,
+        x.ctypes.data, FORMATS[x_dtype], T, dim, row_stride,
         weight.ctypes.data, weight.strides[0] // 4, weight.strides[1] // 4, _ptr(bias),
         conv_states.ctypes.data, conv_states.shape[0], conv_states.strides[0] // 4,
         conv_states.strides[1] // 4, conv_states.strides[2] // 4,

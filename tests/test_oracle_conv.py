@@ -270,6 +270,20 @@ def test_untouched_rows_lines_and_empty_sequences(olib):
         assert np.array_equal(st[line], before[line])
 
 
+def test_no_tokens_at_all(olib):
+    """Page vllm.models.kimi_k3.nvidia.ops.kda_conv, packed_causal_conv1d_fn: with no tokens
+    the call returns at once. Every sequence empty, x with no rows (numpy gives such an
+    array zero strides): the output has no rows and every state word is as it was, also
+    for sequences with an initial state."""
+    wl = make_workload([0, 0, 0], dim=24, part_dim=8, seed=52, init=[True, False, True],
+                       cache_indices=[2, 0, 3], lines=5)
+    assert wl.num_tokens == 0 and wl.x.shape[0] == 0
+    before = wl.conv_states.copy()
+    o, st = oracle.run_workload(wl, lib=olib)
+    assert o.shape == (3, 0, 8)
+    assert np.array_equal(st.view(np.uint32), before.view(np.uint32))
+
+
 def test_rejects_bad_metadata(olib):
     wl = make_workload([3, 4], dim=16, part_dim=8, seed=51)
     bad = wl.query_start_loc.copy()
