@@ -41,8 +41,15 @@ def test_fuzz_bit_exact(seed):
     _compare(wl)
 
 
-@pytest.mark.parametrize("lengths", [[1], [2], [3], [4], [63], [64], [65], [127], [128], [129],
-                                     [0, 5, 0], [1, 1, 1, 1, 1, 1, 1, 1, 1, 1], [200, 1, 64, 3]])
+# One sequence of at most 2048 tokens (or sequences averaging 256 or more) takes 8-row
+# tiles, other calls 16-row tiles: single lengths cover the 8-row edges, the same
+# lengths beside a one-token sequence the 16-row edges, and 2048 / 2049 the switch.
+@pytest.mark.parametrize("lengths", [[1], [2], [3], [4], [7], [8], [9], [15], [16], [17], [63],
+                                     [64], [65], [127], [128], [129], [2048], [2049],
+                                     [15, 1], [16, 1], [17, 1], [31, 1], [32, 1], [33, 1],
+                                     [63, 1], [64, 1], [65, 1], [127, 1], [128, 1], [129, 1],
+                                     [300, 700], [0, 5, 0], [1, 1, 1, 1, 1, 1, 1, 1, 1, 1],
+                                     [200, 1, 64, 3]])
 def test_chunk_edges(lengths):
     from helpers import make_workload
 
